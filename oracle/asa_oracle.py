@@ -1,0 +1,333 @@
+"""Plain float64 CPU oracle for content-aware block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The library and its
+Python binding never call it, and it shares no code with them.
+
+What it computes, in the order the method applies it:
+
+* Attention, dense and masked -- Sparse-vDiT ("Sparse-vDiT: Sparse Attention
+  Acceleration for Video Diffusion Transformers"), section 三 "核心公式":
+  full attention softmax(Q_h K_h^T / sqrt(d)) V_h per head, and the masked form
+  Attention(Q, K, V, M) whose mask M keeps or drops (query-block, key-block)
+  tiles.
+* Static mask sources -- same page, the "四种注意力模式" table: M0 full,
+  M1 skip (output set to zero), M2 diagonal (intra-frame), M3 multi-diagonal
+  (evenly spaced diagonals, cross-frame), M4 vertical stripe (global tokens).
+* Adaptive mask source -- BLADE ("BLADE: Block-Sparse Attention Meets Step
+  Distillation for Efficient Video Generation"), abstract: ASA generates a
+  content-aware block mask per input.  The pages give no rule, so this oracle
+  implements the stated rule: mean-pool Q and K per block, block scores
+  Qp Kp^T / sqrt(d), row softmax, keep the top-k blocks (or the shortest prefix
+  whose probability mass reaches tau, optionally capped), plus the diagonal
+  block and any block holding text tokens.
+
+Parity pins: every function here is checked by ``tests/test_oracle_*.py``
+against closed forms, library routines (torch SDPA, scipy softmax) and brute
+force.  The pooled-score rule and the tuned top-k are specification choices:
+their fidelity to BLADE's own ASA is parity unpinned (the pages do not state
+it).
+
+All arithmetic is float64.  Tensors are NumPy arrays laid out [B, H, N, d].
+"""
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+# Integer codes shared with the C ABI by convention (each side defines them).
+ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE = 0, 1, 2, 3, 4, 5
+TOPK, TAU = 0, 1
+
+AMBIGUITY_GAP = 1e-6
+
+
+# --------------------------------------------------------------------------- blocks
+def num_blocks(N: int, blk: int) -> int:
+    return (N + blk - 1) // blk
+
+
+def block_range(r: int, N: int, blk: int) -> Tuple[int, int]:
+    """Token range [lo, hi) of block r; the last block may be partial."""
+    lo = r * blk
+    return lo, min(lo + blk, N)
+
+
+# --------------------------------------------------------------------------- mask rule
+def pool(X: np.ndarray, blk: int) -> np.ndarray:
+    """Per-block mean of X over the valid tokens of each block.
+
+    X [B,H,N,d] -> [B,H,Nb,d].  A partial last block is averaged over its own
+    token count (no zero padding).
+    """
+    B, H, N, d = X.shape
+    Nb = num_blocks(N, blk)
+    out = np.empty((B, H, Nb, d), dtype=np.float64)
+    for r in range(Nb):
+        lo, hi = block_range(r, N, blk)
+        out[:, :, r, :] = X[:, :, lo:hi, :].astype(np.float64).mean(axis=2)
+    return out
+
+
+def block_scores(Qp: np.ndarray, Kp: np.ndarray) -> np.ndarray:
+    """S[r, c] = Qp[r] . Kp[c] / sqrt(d), the same scale as token attention."""
+    d = Qp.shape[-1]
+    return np.matmul(Qp, np.swapaxes(Kp, -1, -2)) / np.sqrt(d)
+
+
+def block_softmax(S: np.ndarray) -> np.ndarray:
+    """Row softmax over all key blocks (max-subtracted)."""
+    m = S.max(axis=-1, keepdims=True)
+    e = np.exp(S - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def rank_order(p_row: np.ndarray) -> np.ndarray:
+    """Key-block indices sorted by probability descending, ties by smaller index."""
+    idx = np.arange(p_row.shape[0])
+    return np.lexsort((idx, -p_row))
+
+
+def adaptive_count(p_row: np.ndarray, order: np.ndarray, mode: int, k: int,
+                   tau: float, k_cap: int) -> int:
+    """How many leading entries of the rank order the adaptive source keeps."""
+    Nb = p_row.shape[0]
+    if mode == TOPK:
+        return min(max(k, 0), Nb)
+    if mode == TAU:
+        mass = 0.0
+        m = Nb
+        for t in range(Nb):
+            mass += p_row[order[t]]          # sequential prefix sum, rank order
+            if mass >= tau:
+                m = t + 1
+                break
+        if k_cap > 0:
+            m = min(m, k_cap)
+        return m
+    raise ValueError(f"unknown adaptive mode {mode}")
+
+
+def adaptive_set(p_row: np.ndarray, mode: int, k: int, tau: float, k_cap: int) -> np.ndarray:
+    order = rank_order(p_row)
+    m = adaptive_count(p_row, order, mode, k, tau, k_cap)
+    return np.sort(order[:m])
+
+
+def text_blocks(Nb: int, blk: int, n_text: int) -> int:
+    """Number of leading blocks that hold at least one text token."""
+    if n_text <= 0:
+        return 0
+    return min(Nb, num_blocks(n_text, blk))
+
+
+def static_row(pattern: int, param: int, r: int, N: int, blk: int) -> np.ndarray:
+    """Boolean row of kept key blocks for one static pattern (block level).
+
+    MULTIDIAG(S): tile (r, c) is kept iff some query i in block r and key j in
+    block c satisfy (j - i) = 0 mod S, i.e. the integer interval
+    [min T_c - max T_r, max T_c - min T_r] contains a multiple of S.
+    """
+    Nb = num_blocks(N, blk)
+    row = np.zeros(Nb, dtype=bool)
+    if pattern == FULL:
+        row[:] = True
+    elif pattern == SKIP:
+        pass
+    elif pattern == DIAG:
+        row[r] = True
+    elif pattern == VSTRIPE:
+        row[:max(0, min(param, Nb))] = True
+    elif pattern == MULTIDIAG:
+        S = int(param)
+        if S <= 0:
+            raise ValueError("multi-diagonal stride must be positive")
+        qlo, qhi = block_range(r, N, blk)
+        for c in range(Nb):
+            klo, khi = block_range(c, N, blk)
+            lo = klo - (qhi - 1)
+            hi = (khi - 1) - qlo
+            # smallest multiple of S that is >= lo, compared with hi
+            first = -((-lo) // S) * S
+            row[c] = first <= hi
+    else:
+        raise ValueError(f"unknown pattern id {pattern}")
+    return row
+
+
+def static_mask(B: int, H: int, N: int, blk: int,
+                patterns: Sequence[Tuple[int, int]]) -> np.ndarray:
+    """Block mask [B,H,Nb,Nb] from per-head static patterns alone."""
+    Nb = num_blocks(N, blk)
+    M = np.zeros((B, H, Nb, Nb), dtype=bool)
+    cache: Dict[Tuple[int, int], np.ndarray] = {}
+    for h in range(H):
+        pid, prm = patterns[h]
+        if pid == ADAPTIVE:
+            raise ValueError("the static call takes no adaptive heads")
+        if (pid, prm) not in cache:
+            cache[(pid, prm)] = np.stack([static_row(pid, prm, r, N, blk) for r in range(Nb)])
+        M[:, h] = cache[(pid, prm)]
+    return M
+
+
+def build_mask(Q: np.ndarray, K: np.ndarray, blk: int, *, mode: int, k: int = 0,
+               tau: float = 0.0, k_cap: int = 0, n_text: int = 0, keep_diag: int = 1,
+               patterns: Optional[Sequence[Tuple[int, int]]] = None,
+               return_details: bool = False):
+    """Adaptive block mask [B,H,Nb,Nb] (bool), unioned with forced and static blocks.
+
+    kept_r = A_r  U  {r if keep_diag}  U  {text key blocks}  U  static_r(head),
+    a row whose query block holds text tokens is full, and a SKIP head is empty.
+    """
+    B, H, N, d = Q.shape
+    Nb = num_blocks(N, blk)
+    Qp, Kp = pool(Q, blk), pool(K, blk)
+    S = block_scores(Qp, Kp)
+    P = block_softmax(S)
+    nt = text_blocks(Nb, blk, n_text)
+    pats = list(patterns) if patterns is not None else [(ADAPTIVE, 0)] * H
+    M = np.zeros((B, H, Nb, Nb), dtype=bool)
+    counts = np.zeros((B, H, Nb), dtype=np.int64)
+    static_cache: Dict[Tuple[int, int, int], np.ndarray] = {}
+    for b in range(B):
+        for h in range(H):
+            pid, prm = pats[h]
+            if pid == SKIP:
+                continue
+            for r in range(Nb):
+                row = np.zeros(Nb, dtype=bool)
+                order = rank_order(P[b, h, r])
+                m = adaptive_count(P[b, h, r], order, mode, k, tau, k_cap)
+                counts[b, h, r] = m
+                row[order[:m]] = True
+                if keep_diag:
+                    row[r] = True
+                row[:nt] = True
+                if r < nt:
+                    row[:] = True
+                if pid != ADAPTIVE:
+                    key = (pid, prm, r)
+                    if key not in static_cache:   # static rows do not depend on the head
+                        static_cache[key] = static_row(pid, prm, r, N, blk)
+                    row |= static_cache[key]
+                M[b, h, r] = row
+    if return_details:
+        return M, {"Qp": Qp, "Kp": Kp, "S": S, "P": P, "adaptive_count": counts}
+    return M
+
+
+def ambiguous_rows(S: np.ndarray, P: np.ndarray, *, mode: int, k: int = 0, tau: float = 0.0,
+                   k_cap: int = 0, gap: float = AMBIGUITY_GAP) -> np.ndarray:
+    """Rows whose adaptive selection could flip under rounding-order differences.
+
+    A row is ambiguous if the last kept and first dropped candidates of the rank
+    order differ in block score by less than ``gap``, or (cumulative-mass mode)
+    the prefix mass just before or at the stopping point is within ``gap`` of tau.
+    Returns a bool array [B,H,Nb].
+    """
+    B, H, Nb, _ = S.shape
+    amb = np.zeros((B, H, Nb), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for r in range(Nb):
+                p = P[b, h, r]
+                order = rank_order(p)
+                m = adaptive_count(p, order, mode, k, tau, k_cap)
+                flag = False
+                if 0 < m < Nb:
+                    flag = abs(S[b, h, r, order[m - 1]] - S[b, h, r, order[m]]) < gap
+                if mode == TAU and not flag:
+                    cs = np.cumsum(p[order])
+                    for t in (m - 2, m - 1):
+                        if 0 <= t < Nb and abs(cs[t] - tau) < gap:
+                            flag = True
+                amb[b, h, r] = flag
+    return amb
+
+
+def to_csr(M: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Row-major CSR of a [B,H,Nb,Nb] block mask: row_ptr [B*H*Nb+1], col_idx ascending."""
+    rows = M.reshape(-1, M.shape[-1])
+    counts = rows.sum(axis=1)
+    row_ptr = np.zeros(rows.shape[0] + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.nonzero(rows)[1].astype(np.int64)   # row-major, ascending per row
+    return row_ptr, col_idx
+
+
+def density(M: np.ndarray, heads: Optional[Sequence[int]] = None) -> float:
+    """Fraction of kept tiles (1 - sparsity S_i in the Sparse-vDiT search loss)."""
+    if heads is not None:
+        M = M[:, list(heads)]
+    return float(M.mean())
+
+
+# --------------------------------------------------------------------------- attention
+def _row_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """softmax(q k^T / sqrt(d)) v for a set of query rows, two-pass per row."""
+    d = q.shape[-1]
+    s = (q @ k.T) / np.sqrt(d)
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return (e @ v) / e.sum(axis=1, keepdims=True)
+
+
+def kept_tokens(mask_row: np.ndarray, N: int, blk: int) -> np.ndarray:
+    """J = union of the token ranges of the kept key blocks (ascending)."""
+    parts = [np.arange(*block_range(c, N, blk)) for c in np.nonzero(mask_row)[0]]
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate(parts)
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray, blk: int) -> np.ndarray:
+    """Masked block-sparse attention, float64.  O_i = 0 where no key block is kept."""
+    B, H, N, d = Q.shape
+    Nb = num_blocks(N, blk)
+    O = np.zeros((B, H, N, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(Nb):
+                J = kept_tokens(M[b, h, r], N, blk)
+                if J.size == 0:
+                    continue
+                lo, hi = block_range(r, N, blk)
+                O[b, h, lo:hi] = _row_attention(
+                    Q[b, h, lo:hi].astype(np.float64), K[b, h, J].astype(np.float64),
+                    V[b, h, J].astype(np.float64))
+    return O
+
+
+def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray, blk: int,
+                   rows: Sequence[Tuple[int, int, int]]) -> np.ndarray:
+    """Outputs for selected query tokens (b, h, i) only: [len(rows), d]."""
+    N, d = Q.shape[2], Q.shape[3]
+    out = np.zeros((len(rows), d), dtype=np.float64)
+    for n, (b, h, i) in enumerate(rows):
+        J = kept_tokens(M[b, h, i // blk], N, blk)
+        if J.size == 0:
+            continue
+        out[n] = _row_attention(Q[b, h, i:i + 1].astype(np.float64),
+                                K[b, h, J].astype(np.float64),
+                                V[b, h, J].astype(np.float64))[0]
+    return out
+
+
+def dense_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Full attention (pattern M0) for every head."""
+    B, H, N, d = Q.shape
+    O = np.empty((B, H, N, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            O[b, h] = _row_attention(Q[b, h].astype(np.float64), K[b, h].astype(np.float64),
+                                     V[b, h].astype(np.float64))
+    return O
+
+
+def kept_tile_flops(M: np.ndarray, N: int, blk: int, d: int) -> float:
+    """Sum over kept tiles of 4 * n_r * n_c * d (QK^T and PV multiply-adds, x2)."""
+    Nb = M.shape[-1]
+    sizes = np.array([block_range(c, N, blk)[1] - block_range(c, N, blk)[0]
+                      for c in range(Nb)], dtype=np.float64)
+    per_tile = 4.0 * np.outer(sizes, sizes) * d
+    return float((M * per_tile).sum())

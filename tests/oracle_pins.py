@@ -1,0 +1,304 @@
+"""Pins for the float64 oracle: closed forms, library routines and brute force.
+
+Each ``check_*`` function raises AssertionError when the oracle disagrees with
+something fixed independently of it.  ``test_oracle_pins.py`` runs them on the
+oracle as written; ``test_oracle_mutations.py`` plants plausible mistakes in the
+oracle (on the CPU) and confirms that at least one check catches each.
+"""
+import itertools
+import math
+
+import numpy as np
+import scipy.special
+import torch
+
+import oracle as O
+
+RNG = np.random.default_rng
+
+
+def _qkv(B, H, N, d, seed, scale=1.0):
+    rng = RNG(seed)
+    return tuple(rng.standard_normal((B, H, N, d)) * scale for _ in range(3))
+
+
+def _sdpa(q, k, v):
+    """torch scaled_dot_product_attention in float64 on the CPU (library routine)."""
+    t = [torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v)]
+    return torch.nn.functional.scaled_dot_product_attention(*t).numpy()
+
+
+# ------------------------------------------------------------------ attention pins
+def check_dense_equals_sdpa():
+    """All-ones block mask == full attention (torch SDPA, float64), ragged N."""
+    q, k, v = _qkv(1, 2, 200, 16, 11)
+    M = np.ones((1, 2, O.num_blocks(200, 64), O.num_blocks(200, 64)), dtype=bool)
+    ref = _sdpa(q, k, v)
+    assert np.allclose(O.attention(q, k, v, M, 64), ref, atol=1e-12, rtol=0)
+    assert np.allclose(O.dense_attention(q, k, v), ref, atol=1e-12, rtol=0)
+
+
+def check_block_diagonal_equals_independent_blocks():
+    """Diagonal-only mask == attention run separately inside each block."""
+    N, blk = 150, 32
+    q, k, v = _qkv(1, 3, N, 8, 12)
+    M = O.static_mask(1, 3, N, blk, [(O.DIAG, 0)] * 3)
+    out = O.attention(q, k, v, M, blk)
+    for r in range(O.num_blocks(N, blk)):
+        lo, hi = O.block_range(r, N, blk)
+        ref = _sdpa(q[:, :, lo:hi], k[:, :, lo:hi], v[:, :, lo:hi])
+        assert np.allclose(out[:, :, lo:hi], ref, atol=1e-12, rtol=0)
+
+
+def check_weights_sum_to_one():
+    """With V = 1 every non-empty output row is exactly 1 (weights sum to 1)."""
+    N, blk, d = 300, 64, 16
+    rng = RNG(13)
+    q = rng.standard_normal((1, 2, N, d)) * 3
+    k = rng.standard_normal((1, 2, N, d)) * 3
+    v = np.ones((1, 2, N, d))
+    Nb = O.num_blocks(N, blk)
+    M = rng.random((1, 2, Nb, Nb)) < 0.5
+    M[0, 0, 1, :] = False                                   # one empty row
+    out = O.attention(q, k, v, M, blk)
+    for h in range(2):
+        for r in range(Nb):
+            lo, hi = O.block_range(r, N, blk)
+            want = 1.0 if M[0, h, r].any() else 0.0
+            assert np.allclose(out[0, h, lo:hi], want, atol=1e-12, rtol=0)
+
+
+def check_identical_keys_give_mean_of_v():
+    """One kept key block whose keys are identical => uniform weights => mean(V_block)."""
+    N, blk, d = 256, 64, 16
+    rng = RNG(14)
+    q = rng.standard_normal((1, 1, N, d))
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    Nb = O.num_blocks(N, blk)
+    for c in range(Nb):
+        lo, hi = O.block_range(c, N, blk)
+        k[0, 0, lo:hi] = rng.standard_normal(d)             # all keys of block c equal
+    M = np.zeros((1, 1, Nb, Nb), dtype=bool)
+    pick = [(r * 3 + 1) % Nb for r in range(Nb)]
+    for r in range(Nb):
+        M[0, 0, r, pick[r]] = True
+    out = O.attention(q, k, v, M, blk)
+    for r in range(Nb):
+        lo, hi = O.block_range(r, N, blk)
+        klo, khi = O.block_range(pick[r], N, blk)
+        assert np.allclose(out[0, 0, lo:hi], v[0, 0, klo:khi].mean(axis=0), atol=1e-12, rtol=0)
+
+
+def check_bruteforce_2head_n128():
+    """2 heads, N=128, ragged blocks (48, 48, 32): pure-Python loops with math.exp."""
+    N, blk, d, H = 128, 48, 8, 2
+    rng = RNG(15)
+    q, k, v = (rng.standard_normal((1, H, N, d)) for _ in range(3))
+    Nb = O.num_blocks(N, blk)
+    M = rng.random((1, H, Nb, Nb)) < 0.6
+    M[0, 1, 2, :] = False
+    out = O.attention(q, k, v, M, blk)
+    for h in range(H):
+        for i in range(N):
+            r = i // blk
+            js = [j for j in range(N) if M[0, h, r, j // blk]]
+            if not js:
+                assert all(out[0, h, i, t] == 0.0 for t in range(d))
+                continue
+            s = [sum(q[0, h, i, t] * k[0, h, j, t] for t in range(d)) / math.sqrt(d) for j in js]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            z = sum(w)
+            for t in range(d):
+                o = sum(w[n] * v[0, h, js[n], t] for n in range(len(js))) / z
+                assert abs(o - out[0, h, i, t]) < 1e-12
+
+
+def check_skip_and_empty_rows_are_zero():
+    N, blk = 256, 64
+    q, k, v = _qkv(1, 2, N, 8, 16)
+    M = O.static_mask(1, 2, N, blk, [(O.SKIP, 0), (O.FULL, 0)])
+    out = O.attention(q, k, v, M, blk)
+    assert np.all(out[0, 0] == 0.0)
+    assert np.allclose(out[0, 1], _sdpa(q[:, 1:2], k[:, 1:2], v[:, 1:2])[0, 0], atol=1e-12)
+
+
+def check_attention_rows_match_full():
+    N, blk = 200, 64
+    q, k, v = _qkv(1, 2, N, 8, 17)
+    Nb = O.num_blocks(N, blk)
+    M = RNG(17).random((1, 2, Nb, Nb)) < 0.5
+    full = O.attention(q, k, v, M, blk)
+    rows = [(0, h, i) for h in range(2) for i in (0, 63, 64, 150, 199)]
+    got = O.attention_rows(q, k, v, M, blk, rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.allclose(got[n], full[b, h, i], atol=1e-13, rtol=0)
+
+
+# ------------------------------------------------------------------ mask-rule pins
+def check_pool_score_bilinearity():
+    """S[r,c] == mean over token pairs (i in T_r, j in T_c) of q_i.k_j / sqrt(d)."""
+    N, blk, d = 70, 16, 5                                   # last block has 6 tokens
+    rng = RNG(21)
+    q = rng.standard_normal((1, 1, N, d))
+    k = rng.standard_normal((1, 1, N, d)) + 0.5
+    S = O.block_scores(O.pool(q, blk), O.pool(k, blk))
+    Nb = O.num_blocks(N, blk)
+    for r in range(Nb):
+        for c in range(Nb):
+            tot, cnt = 0.0, 0
+            for i in range(*O.block_range(r, N, blk)):
+                for j in range(*O.block_range(c, N, blk)):
+                    tot += sum(q[0, 0, i, t] * k[0, 0, j, t] for t in range(d)) / math.sqrt(d)
+                    cnt += 1
+            assert abs(S[0, 0, r, c] - tot / cnt) < 1e-12
+
+
+def check_block_softmax_matches_scipy():
+    S = RNG(22).standard_normal((2, 3, 7, 7)) * 5
+    assert np.allclose(O.block_softmax(S), scipy.special.softmax(S, axis=-1), atol=1e-15, rtol=1e-13)
+
+
+def check_rank_order_ties():
+    p = np.array([0.1, 0.3, 0.1, 0.3, 0.2])
+    assert list(O.rank_order(p)) == [1, 3, 4, 0, 2]
+
+
+def _subset_masses(p):
+    Nb = len(p)
+    for m in range(Nb + 1):
+        for sub in itertools.combinations(range(Nb), m):
+            yield m, sub, sum(p[list(sub)]) if sub else 0.0
+
+
+def check_selection_bruteforce():
+    """Top-k and tau-prefix against exhaustive subset enumeration (Nb <= 8)."""
+    rng = RNG(23)
+    for trial in range(40):
+        Nb = int(rng.integers(1, 9))
+        p = scipy.special.softmax(rng.standard_normal(Nb) * 2)
+        for k in range(0, Nb + 2):
+            got = set(O.adaptive_set(p, O.TOPK, k, 0.0, 0).tolist())
+            kk = min(k, Nb)
+            best = max((s for m, s, w in _subset_masses(p) if m == kk),
+                       key=lambda s: sum(p[list(s)]) if s else 0.0)
+            assert got == set(best)
+        for tau in (0.05, 0.3, 0.5, 0.75, 0.9, 0.99):
+            got = O.adaptive_set(p, O.TAU, 0, tau, 0)
+            feasible = [(m, s, w) for m, s, w in _subset_masses(p) if w >= tau]
+            mmin = min(m for m, s, w in feasible)
+            assert len(got) == mmin
+            best_w = max(w for m, s, w in feasible if m == mmin)
+            assert abs(sum(p[got]) - best_w) < 1e-12
+            for cap in (1, 2, 3):
+                capped = O.adaptive_set(p, O.TAU, 0, tau, cap)
+                assert len(capped) == min(mmin, cap)
+                # the capped prefix is the top-`len` set
+                assert set(capped.tolist()) == set(O.adaptive_set(p, O.TOPK, len(capped), 0, 0).tolist())
+
+
+def check_selection_limits_and_monotone():
+    rng = RNG(24)
+    for trial in range(20):
+        Nb = int(rng.integers(2, 40))
+        p = scipy.special.softmax(rng.standard_normal(Nb) * 3)
+        assert len(O.adaptive_set(p, O.TOPK, Nb, 0, 0)) == Nb
+        assert len(O.adaptive_set(p, O.TOPK, Nb + 5, 0, 0)) == Nb
+        assert len(O.adaptive_set(p, O.TAU, 0, 1.0 + 1e-9, 0)) == Nb
+        prev = set()
+        for k in range(Nb + 1):
+            cur = set(O.adaptive_set(p, O.TOPK, k, 0, 0).tolist())
+            assert prev <= cur and len(cur) == k
+            prev = cur
+        prev = set()
+        for tau in np.linspace(0.01, 1.0, 30):
+            cur = set(O.adaptive_set(p, O.TAU, 0, float(tau), 0).tolist())
+            assert prev <= cur
+            prev = cur
+
+
+def check_forced_blocks():
+    """Diagonal kept, text key blocks kept, text query rows full, skip head empty."""
+    N, blk, n_text = 600, 64, 100                            # text spans blocks 0 and 1
+    rng = RNG(25)
+    q = rng.standard_normal((1, 3, N, 8))
+    k = rng.standard_normal((1, 3, N, 8))
+    M = O.build_mask(q, k, blk, mode=O.TOPK, k=1, n_text=n_text, keep_diag=1,
+                     patterns=[(O.ADAPTIVE, 0), (O.VSTRIPE, 4), (O.SKIP, 0)])
+    Nb = O.num_blocks(N, blk)
+    for h in range(2):
+        assert M[0, h, 0].all() and M[0, h, 1].all()         # text rows
+        for r in range(Nb):
+            assert M[0, h, r, r] and M[0, h, r, 0] and M[0, h, r, 1]
+    assert M[0, 1, :, :4].all()                              # static stripe unioned
+    assert not M[0, 2].any()
+    # rows outside text keep exactly top-1 U diag U text columns (U stripe)
+    M0 = O.build_mask(q, k, blk, mode=O.TOPK, k=1, n_text=0, keep_diag=0)
+    assert (M0.sum(axis=-1) == 1).all()
+
+
+def check_static_patterns_token_pairs():
+    """Closed-form static rows vs token-pair enumeration, ragged and strided cases."""
+    for N, blk in ((300, 32), (256, 64), (130, 16)):
+        Nb = O.num_blocks(N, blk)
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        for S in (1, 5, 16, 32, 48, 100, 128, 1000):
+            tok = ((j - i) % S) == 0
+            for r in range(Nb):
+                ql, qh = O.block_range(r, N, blk)
+                want = np.array([tok[ql:qh, slice(*O.block_range(c, N, blk))].any()
+                                 for c in range(Nb)])
+                assert np.array_equal(O.static_row(O.MULTIDIAG, S, r, N, blk), want), (N, blk, S, r)
+        tokd = (i == j)
+        for r in range(Nb):
+            ql, qh = O.block_range(r, N, blk)
+            want = np.array([tokd[ql:qh, slice(*O.block_range(c, N, blk))].any() for c in range(Nb)])
+            assert np.array_equal(O.static_row(O.DIAG, 0, r, N, blk), want)
+            assert np.array_equal(O.static_row(O.MULTIDIAG, N + 7, r, N, blk), want)
+            assert O.static_row(O.VSTRIPE, Nb, r, N, blk).all()
+            assert O.static_row(O.FULL, 0, r, N, blk).all()
+            assert not O.static_row(O.SKIP, 0, r, N, blk).any()
+            s2 = O.static_row(O.VSTRIPE, 2, r, N, blk)
+            assert s2[:2].all() and not s2[2:].any()
+
+
+def check_static_counts_8192():
+    """Frame-stride multi-diagonal at N=8192, blk=128: 8 tiles per row; stripe 2; diag 1."""
+    pats = [(O.DIAG, 0), (O.MULTIDIAG, 1024), (O.VSTRIPE, 2), (O.FULL, 0), (O.SKIP, 0)]
+    M = O.static_mask(1, 5, 8192, 128, pats)
+    counts = M.sum(axis=-1)[0]
+    assert (counts[0] == 1).all() and (counts[1] == 8).all() and (counts[2] == 2).all()
+    assert (counts[3] == 64).all() and (counts[4] == 0).all()
+
+
+def check_csr_layout():
+    rng = RNG(26)
+    M = rng.random((2, 3, 9, 9)) < 0.3
+    row_ptr, col_idx = O.to_csr(M)
+    rows = M.reshape(-1, 9)
+    assert row_ptr[0] == 0 and len(row_ptr) == rows.shape[0] + 1
+    for n in range(rows.shape[0]):
+        cols = col_idx[row_ptr[n]:row_ptr[n + 1]]
+        assert list(cols) == [c for c in range(9) if rows[n, c]]
+
+
+def check_kept_tile_flops():
+    N, blk, d = 100, 32, 4
+    Nb = O.num_blocks(N, blk)
+    M = RNG(27).random((1, 1, Nb, Nb)) < 0.5
+    pairs = sum(1 for i in range(N) for j in range(N) if M[0, 0, i // blk, j // blk])
+    assert O.kept_tile_flops(M, N, blk, d) == 4.0 * pairs * d
+
+
+ALL_CHECKS = [
+    check_dense_equals_sdpa, check_block_diagonal_equals_independent_blocks,
+    check_weights_sum_to_one, check_identical_keys_give_mean_of_v,
+    check_bruteforce_2head_n128, check_skip_and_empty_rows_are_zero,
+    check_attention_rows_match_full, check_pool_score_bilinearity,
+    check_block_softmax_matches_scipy, check_rank_order_ties, check_selection_bruteforce,
+    check_selection_limits_and_monotone, check_forced_blocks,
+    check_static_patterns_token_pairs, check_static_counts_8192, check_csr_layout,
+    check_kept_tile_flops,
+]

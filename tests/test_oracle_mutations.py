@@ -1,0 +1,121 @@
+"""Plant plausible mistakes in the oracle (CPU only) and require a pin to catch each.
+
+This guards the pins themselves: a mistake of the kind listed here (a dropped
+term, a wrong scale, a wrong tie-break, an off-by-one, a zero-padded partial
+block, a transposed operand) must fail at least one ``check_*`` function.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.asa_oracle as core
+from oracle_pins import ALL_CHECKS
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(core, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+def _pool_sum(X, blk):
+    B, H, N, d = X.shape
+    Nb = core.num_blocks(N, blk)
+    out = np.empty((B, H, Nb, d))
+    for r in range(Nb):
+        lo, hi = core.block_range(r, N, blk)
+        out[:, :, r] = X[:, :, lo:hi].sum(axis=2)
+    return out
+
+
+def _pool_zero_padded(X, blk):
+    B, H, N, d = X.shape
+    Nb = core.num_blocks(N, blk)
+    out = np.empty((B, H, Nb, d))
+    for r in range(Nb):
+        lo, hi = core.block_range(r, N, blk)
+        out[:, :, r] = X[:, :, lo:hi].sum(axis=2) / blk
+    return out
+
+
+def _scores_unscaled(Qp, Kp):
+    return np.matmul(Qp, np.swapaxes(Kp, -1, -2))
+
+
+def _softmax_wrong_axis(S):
+    e = np.exp(S - S.max(axis=-2, keepdims=True))
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _rank_ties_larger_first(p):
+    idx = np.arange(p.shape[0])
+    return np.lexsort((-idx, -p))
+
+
+_orig_count = core.adaptive_count
+
+
+def _count_off_by_one(p, order, mode, k, tau, k_cap):
+    m = _orig_count(p, order, mode, k, tau, k_cap)
+    return min(m + 1, p.shape[0]) if mode == core.TAU else m
+
+
+def _row_attention_noscale(q, k, v):
+    s = q @ k.T
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e @ v) / e.sum(axis=1, keepdims=True)
+
+
+def _kept_tokens_full_blocks_only(mask_row, N, blk):
+    parts = [np.arange(c * blk, c * blk + blk) for c in np.nonzero(mask_row)[0]
+             if c * blk + blk <= N]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+_orig_static = core.static_row
+
+
+def _static_floor(pattern, param, r, N, blk):
+    if pattern != core.MULTIDIAG:
+        return _orig_static(pattern, param, r, N, blk)
+    Nb = core.num_blocks(N, blk)
+    row = np.zeros(Nb, dtype=bool)
+    qlo, qhi = core.block_range(r, N, blk)
+    for c in range(Nb):
+        klo, khi = core.block_range(c, N, blk)
+        lo, hi = klo - (qhi - 1), (khi - 1) - qlo
+        row[c] = (lo // param) * param <= hi          # floor instead of ceiling
+    return row
+
+
+def _row_attention_no_normalise(q, k, v):
+    s = (q @ k.T) / np.sqrt(q.shape[-1])
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return e @ v
+
+
+MUTATIONS = {
+    "pool_sum_not_mean": ("pool", _pool_sum),
+    "pool_zero_padded_partial_block": ("pool", _pool_zero_padded),
+    "block_scores_missing_scale": ("block_scores", _scores_unscaled),
+    "block_softmax_wrong_axis": ("block_softmax", _softmax_wrong_axis),
+    "rank_ties_larger_index_first": ("rank_order", _rank_ties_larger_first),
+    "tau_prefix_off_by_one": ("adaptive_count", _count_off_by_one),
+    "attention_missing_scale": ("_row_attention", _row_attention_noscale),
+    "attention_drops_partial_key_block": ("kept_tokens", _kept_tokens_full_blocks_only),
+    "multidiag_floor_not_ceiling": ("static_row", _static_floor),
+    "attention_not_normalised": ("_row_attention", _row_attention_no_normalise),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(monkeypatch, name):
+    attr, fn = MUTATIONS[name]
+    _patch(monkeypatch, attr, fn)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check()
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"planted mistake {name} went unnoticed by every pin"
