@@ -1,0 +1,225 @@
+"""Python binding of libasa.so: content-aware block-sparse attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the library's HIP
+kernels; torch supplies device memory and the current stream.  There is no CPU
+fallback: importing this package fails if the built library is missing.
+
+Entry points (same names as the C ABI in include/asa.h):
+    asa_build_mask(q, k, blk, mode, ...)   -> (row_ptr, col_idx)
+    asa_static_mask(B, H, N, blk, patterns, device) -> (row_ptr, col_idx)
+    asa_attention_fwd(q, k, v, row_ptr, col_idx, blk, ...) -> O
+"""
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libasa.so")
+
+ASA_F32, ASA_BF16 = 0, 1
+ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE = 0, 1, 2, 3, 4, 5
+TOPK, TAU = 0, 1
+
+
+class asa_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("blk", ctypes.c_int32), ("in_dtype", ctypes.c_int32)]
+
+
+class asa_adaptive(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("k", ctypes.c_int32), ("tau", ctypes.c_double),
+                ("k_cap", ctypes.c_int32), ("n_text", ctypes.c_int32), ("keep_diag", ctypes.c_int32)]
+
+
+class asa_head_pattern(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int32), ("param", ctypes.c_int32)]
+
+
+class asa_csr(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+
+
+EXPORTS = {
+    "asa_version": (ctypes.c_int32, []),
+    "asa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "asa_last_error": (ctypes.c_char_p, []),
+    "asa_csr_capacity": (ctypes.c_int64, [ctypes.POINTER(asa_shape)]),
+    "asa_build_mask_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(asa_shape)]),
+    "asa_static_mask_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(asa_shape)]),
+    "asa_build_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(asa_shape),
+                                      ctypes.POINTER(asa_adaptive), ctypes.POINTER(asa_head_pattern),
+                                      ctypes.POINTER(asa_csr), ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]),
+    "asa_static_mask": (ctypes.c_int, [ctypes.POINTER(asa_shape), ctypes.POINTER(asa_head_pattern),
+                                       ctypes.POINTER(asa_csr), ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]),
+    "asa_attention_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.POINTER(asa_shape), ctypes.POINTER(asa_csr),
+                                         ctypes.POINTER(asa_head_pattern), ctypes.c_float, ctypes.c_void_p]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_sparse_attention_asa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class AsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib.asa_last_error().decode(errors="replace")
+        name = lib.asa_status_string(status).decode()
+        super().__init__(f"{where}: {name} ({status}): {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise AsaError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ASA_BF16
+    if t.dtype == torch.float32:
+        return ASA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _shape_of(q: torch.Tensor, blk: int) -> asa_shape:
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    return asa_shape(B, H, N, d, blk, _dtype_code(q))
+
+
+def _patterns(patterns: Optional[Sequence[Tuple[int, int]]], H: int):
+    if patterns is None:
+        return None
+    if len(patterns) != H:
+        raise ValueError(f"need {H} head patterns, got {len(patterns)}")
+    arr = (asa_head_pattern * H)()
+    for h, (pid, prm) in enumerate(patterns):
+        arr[h].id, arr[h].param = int(pid), int(prm)
+    return arr
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require_device(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def num_blocks(N: int, blk: int) -> int:
+    return (N + blk - 1) // blk
+
+
+def asa_csr_capacity(B: int, H: int, N: int, blk: int) -> int:
+    shp = asa_shape(B, H, N, 64, blk, ASA_BF16)
+    return int(lib.asa_csr_capacity(ctypes.byref(shp)))
+
+
+def _alloc_csr(B, H, N, blk, device):
+    shp = asa_shape(B, H, N, 64, blk, ASA_BF16)
+    cap = int(lib.asa_csr_capacity(ctypes.byref(shp)))
+    if cap < 0:
+        raise ValueError("invalid shape for a block mask")
+    rows = B * H * num_blocks(N, blk)
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=device)
+    col_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+    return row_ptr, col_idx
+
+
+def asa_build_mask(q: torch.Tensor, k: torch.Tensor, blk: int, mode: int, *, k_top: int = 0,
+                   tau: float = 0.0, k_cap: int = 0, n_text: int = 0, keep_diag: int = 1,
+                   patterns: Optional[Sequence[Tuple[int, int]]] = None,
+                   out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Adaptive block mask (plus forced / static blocks) as CSR (row_ptr, col_idx).
+
+    col_idx is sized for the worst case; its first row_ptr[-1] entries are valid.
+    """
+    _require_device(q, k)
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must have the same shape and dtype")
+    shp = _shape_of(q, blk)
+    B, H, N, _ = q.shape
+    row_ptr, col_idx = out if out is not None else _alloc_csr(B, H, N, blk, q.device)
+    csr = asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+    ad = asa_adaptive(mode, k_top, tau, k_cap, n_text, keep_diag)
+    need = int(lib.asa_build_mask_workspace_size(ctypes.byref(shp)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    pats = _patterns(patterns, H)
+    _check(lib.asa_build_mask(q.data_ptr(), k.data_ptr(), ctypes.byref(shp), ctypes.byref(ad),
+                              pats, ctypes.byref(csr), workspace.data_ptr(), workspace.numel(),
+                              _stream(q.device, stream)), "asa_build_mask")
+    return row_ptr, col_idx
+
+
+def asa_static_mask(B: int, H: int, N: int, blk: int, patterns: Sequence[Tuple[int, int]],
+                    device, *, out=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Static-pattern block mask as CSR (row_ptr, col_idx)."""
+    device = torch.device(device)
+    shp = asa_shape(B, H, N, 64, blk, ASA_BF16)
+    row_ptr, col_idx = out if out is not None else _alloc_csr(B, H, N, blk, device)
+    csr = asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+    need = int(lib.asa_static_mask_workspace_size(ctypes.byref(shp)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    pats = _patterns(patterns, H)
+    if pats is None:
+        raise ValueError("patterns are required")
+    _check(lib.asa_static_mask(ctypes.byref(shp), pats, ctypes.byref(csr), workspace.data_ptr(),
+                               workspace.numel(), _stream(device, stream)), "asa_static_mask")
+    return row_ptr, col_idx
+
+
+def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                      col_idx: torch.Tensor, blk: int, *,
+                      patterns: Optional[Sequence[Tuple[int, int]]] = None,
+                      out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block-sparse attention over the kept tiles of the CSR mask; returns O [B,H,N,d]."""
+    _require_device(q, k, v, row_ptr, col_idx)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    shp = _shape_of(q, blk)
+    B, H, N, d = q.shape
+    if row_ptr.numel() != B * H * num_blocks(N, blk) + 1:
+        raise ValueError("row_ptr length does not match [B, H, Nb] rows")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    _require_device(out)
+    o_code = _dtype_code(out)
+    csr = asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+    pats = _patterns(patterns, H)
+    _check(lib.asa_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), o_code,
+                                 ctypes.byref(shp), ctypes.byref(csr), pats, float(scale),
+                                 _stream(q.device, stream)), "asa_attention_fwd")
+    return out
+
+
+__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_csr_capacity",
+           "AsaError", "lib", "LIB_PATH", "EXPORTS", "num_blocks",
+           "ADAPTIVE", "FULL", "SKIP", "DIAG", "MULTIDIAG", "VSTRIPE", "TOPK", "TAU"]

@@ -1,0 +1,70 @@
+"""Build libasa.so (the C-ABI library with its gfx950 kernels) in-tree with hipcc.
+
+Usage: python -m block_sparse_attention_asa_amd.build  [--verbose]
+Output: block_sparse_attention_asa_amd/libasa.so
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libasa.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+SOURCES = ["asa_api.cpp", "mask.hip", "attn_fwd.hip"]
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-result",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    path = os.path.join(ROCM, "bin", "hipcc")
+    if not os.path.exists(path):
+        raise RuntimeError(f"hipcc not found at {path}")
+    return path
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)   # host pass does not know the feature
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libasa.so atomically; returns the library path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="asa_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            _run([cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        tmp_lib = os.path.join(tmp, "libasa.so")
+        _run([cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp_lib,
+              f"-Wl,-rpath,{ROCM}/lib", f"-L{ROCM}/lib", "-lamdhip64"], verbose)
+        staged = LIB + ".tmp"
+        shutil.copyfile(tmp_lib, staged)
+        os.replace(staged, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

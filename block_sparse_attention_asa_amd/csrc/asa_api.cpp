@@ -1,0 +1,251 @@
+// C ABI entry points: host-side validation, workspace layout and kernel enqueueing.
+// Every check runs before anything is enqueued; no HIP call is made for an invalid call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/asa.h"
+#include "asa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+asa_status fail(asa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+asa_status fail(asa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+asa_status hip_fail(hipError_t e, const char* what) {
+  return fail(ASA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t num_blocks(const asa_shape* s) { return ((int64_t)s->N + s->blk - 1) / s->blk; }
+
+// Shape checks shared by every entry point.  need_mask: Nb must fit the mask kernels.
+asa_status check_shape(const asa_shape* s, bool need_mask) {
+  if (!s) return fail(ASA_ERR_NULL_ARG, "shape is NULL");
+  if (s->B <= 0 || s->H <= 0 || s->N <= 0)
+    return fail(ASA_ERR_BAD_SHAPE, "B=%d H=%d N=%d must be positive", s->B, s->H, s->N);
+  if (s->in_dtype != ASA_F32 && s->in_dtype != ASA_BF16)
+    return fail(ASA_ERR_BAD_DTYPE, "in_dtype=%d is not ASA_F32 or ASA_BF16", s->in_dtype);
+  if (s->d != 64 && s->d != 128) return fail(ASA_ERR_UNSUPPORTED, "d=%d (supported: 64, 128)", s->d);
+  if (s->blk != 64 && s->blk != 128)
+    return fail(ASA_ERR_UNSUPPORTED, "blk=%d (supported: 64, 128)", s->blk);
+  const int64_t Nb = num_blocks(s);
+  const int64_t rows = (int64_t)s->B * s->H * Nb;
+  if (s->H > asa::kMaxHeads)
+    return fail(ASA_ERR_UNSUPPORTED, "H=%d exceeds the per-head table limit %d", s->H, asa::kMaxHeads);
+  if ((int64_t)s->N * s->d >= ((int64_t)1 << 31))
+    return fail(ASA_ERR_BAD_SHAPE, "N*d=%lld overflows int32 token offsets", (long long)s->N * s->d);
+  if (rows >= ((int64_t)1 << 31) - 1) return fail(ASA_ERR_BAD_SHAPE, "B*H*Nb=%lld rows overflow int32", (long long)rows);
+  if (need_mask) {
+    if (Nb > asa::kMaxMaskBlocks)
+      return fail(ASA_ERR_UNSUPPORTED, "Nb=%lld key blocks exceeds the mask builders' limit %d",
+                  (long long)Nb, asa::kMaxMaskBlocks);
+    if (rows * Nb >= ((int64_t)1 << 31) - 1)
+      return fail(ASA_ERR_BAD_SHAPE, "B*H*Nb*Nb=%lld overflows int32 CSR offsets", (long long)(rows * Nb));
+  }
+  return ASA_OK;
+}
+
+asa_status fill_heads(const asa_shape* s, const asa_head_pattern* pats, bool allow_adaptive,
+                      asa::HeadTable* t) {
+  std::memset(t, 0, sizeof(*t));
+  if (!pats) return ASA_OK;
+  const int64_t Nb = num_blocks(s);
+  for (int h = 0; h < s->H; ++h) {
+    const int id = pats[h].id, prm = pats[h].param;
+    switch (id) {
+      case ASA_PAT_ADAPTIVE:
+        if (!allow_adaptive) return fail(ASA_ERR_BAD_PATTERN, "head %d: ASA_PAT_ADAPTIVE in a static-only call", h);
+        break;
+      case ASA_PAT_FULL:
+      case ASA_PAT_SKIP:
+      case ASA_PAT_DIAG:
+        break;
+      case ASA_PAT_MULTIDIAG:
+        if (prm <= 0) return fail(ASA_ERR_BAD_PATTERN, "head %d: multi-diagonal stride %d must be > 0", h, prm);
+        break;
+      case ASA_PAT_VSTRIPE:
+        if (prm < 0) return fail(ASA_ERR_BAD_PATTERN, "head %d: vertical-stripe width %d must be >= 0", h, prm);
+        break;
+      default:
+        return fail(ASA_ERR_BAD_PATTERN, "head %d: unknown pattern id %d", h, id);
+    }
+    t->id[h] = id;
+    t->param[h] = (id == ASA_PAT_VSTRIPE && prm > Nb) ? (int)Nb : prm;
+  }
+  return ASA_OK;
+}
+
+asa::MaskGeom geom_of(const asa_shape* s) {
+  asa::MaskGeom g{};
+  g.B = s->B; g.H = s->H; g.N = s->N; g.d = s->d; g.blk = s->blk;
+  g.Nb = (int)num_blocks(s);
+  g.words = (g.Nb + 31) / 32;
+  return g;
+}
+
+asa_status check_csr_out(const asa_shape* s, const asa_csr* out) {
+  if (!out) return fail(ASA_ERR_NULL_ARG, "csr is NULL");
+  if (!out->row_ptr || !out->col_idx) return fail(ASA_ERR_NULL_ARG, "csr row_ptr/col_idx is NULL");
+  const int64_t need = asa_csr_capacity(s);
+  if (out->capacity < need)
+    return fail(ASA_ERR_CAPACITY, "csr capacity %lld < required %lld", (long long)out->capacity, (long long)need);
+  return ASA_OK;
+}
+
+asa_status check_workspace(void* ws, size_t have, size_t need) {
+  if (!ws) return fail(ASA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (have < need) return fail(ASA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", have, need);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(ASA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  return ASA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t asa_version(void) { return 10000; }
+
+const char* asa_status_string(asa_status st) {
+  switch (st) {
+    case ASA_OK: return "ASA_OK";
+    case ASA_ERR_NULL_ARG: return "ASA_ERR_NULL_ARG";
+    case ASA_ERR_BAD_SHAPE: return "ASA_ERR_BAD_SHAPE";
+    case ASA_ERR_BAD_DTYPE: return "ASA_ERR_BAD_DTYPE";
+    case ASA_ERR_UNSUPPORTED: return "ASA_ERR_UNSUPPORTED";
+    case ASA_ERR_CAPACITY: return "ASA_ERR_CAPACITY";
+    case ASA_ERR_WORKSPACE: return "ASA_ERR_WORKSPACE";
+    case ASA_ERR_BAD_PATTERN: return "ASA_ERR_BAD_PATTERN";
+    case ASA_ERR_BAD_PARAM: return "ASA_ERR_BAD_PARAM";
+    case ASA_ERR_HIP: return "ASA_ERR_HIP";
+  }
+  return "ASA_ERR_UNKNOWN";
+}
+
+const char* asa_last_error(void) { return g_last_error; }
+
+int64_t asa_csr_capacity(const asa_shape* shape) {
+  if (!shape || shape->B <= 0 || shape->H <= 0 || shape->N <= 0 || shape->blk <= 0) return -1;
+  const int64_t Nb = num_blocks(shape);
+  return (int64_t)shape->B * shape->H * Nb * Nb;
+}
+
+size_t asa_build_mask_workspace_size(const asa_shape* shape) {
+  if (check_shape(shape, true) != ASA_OK) return 0;
+  return asa::mask_workspace_layout(geom_of(shape), true, nullptr, nullptr);
+}
+
+size_t asa_static_mask_workspace_size(const asa_shape* shape) {
+  if (check_shape(shape, true) != ASA_OK) return 0;
+  return asa::mask_workspace_layout(geom_of(shape), false, nullptr, nullptr);
+}
+
+asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
+                          const asa_adaptive* ad, const asa_head_pattern* patterns,
+                          const asa_csr* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error[0] = '\0';
+  asa_status st = check_shape(shape, true);
+  if (st != ASA_OK) return st;
+  if (!Q || !K) return fail(ASA_ERR_NULL_ARG, "Q or K is NULL");
+  if (!ad) return fail(ASA_ERR_NULL_ARG, "adaptive parameters are NULL");
+  if (ad->mode != ASA_MODE_TOPK && ad->mode != ASA_MODE_TAU)
+    return fail(ASA_ERR_BAD_PARAM, "adaptive mode %d is not TOPK or TAU", ad->mode);
+  if (ad->mode == ASA_MODE_TOPK && ad->k < 0) return fail(ASA_ERR_BAD_PARAM, "k=%d must be >= 0", ad->k);
+  if (ad->mode == ASA_MODE_TAU && !(ad->tau >= 0.0 && std::isfinite(ad->tau)))
+    return fail(ASA_ERR_BAD_PARAM, "tau=%g must be finite and >= 0", ad->tau);
+  if (ad->k_cap < 0) return fail(ASA_ERR_BAD_PARAM, "k_cap=%d must be >= 0", ad->k_cap);
+  if (ad->n_text < 0 || ad->n_text > shape->N)
+    return fail(ASA_ERR_BAD_PARAM, "n_text=%d must lie in [0, N]", ad->n_text);
+  if (ad->keep_diag != 0 && ad->keep_diag != 1) return fail(ASA_ERR_BAD_PARAM, "keep_diag must be 0 or 1");
+  asa::HeadTable heads;
+  if ((st = fill_heads(shape, patterns, true, &heads)) != ASA_OK) return st;
+  if ((st = check_csr_out(shape, out)) != ASA_OK) return st;
+  const asa::MaskGeom g = geom_of(shape);
+  const size_t need = asa::mask_workspace_layout(g, true, nullptr, nullptr);
+  if ((st = check_workspace(workspace, workspace_bytes, need)) != ASA_OK) return st;
+
+  asa::MaskWorkspace ws;
+  asa::mask_workspace_layout(g, true, &ws, workspace);
+  asa::AdaptiveParams p{};
+  p.mode = ad->mode;
+  p.k = ad->k;
+  p.tau = ad->tau;
+  p.k_cap = ad->k_cap;
+  p.n_text_blocks = ad->n_text > 0 ? (int)((ad->n_text + shape->blk - 1) / shape->blk) : 0;
+  p.keep_diag = ad->keep_diag;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = asa::launch_pool(Q, K, shape->in_dtype == ASA_BF16, g, ws, s)) != hipSuccess) return hip_fail(e, "pool");
+  if ((e = asa::launch_scores(g, ws, s)) != hipSuccess) return hip_fail(e, "scores");
+  if ((e = asa::launch_select(g, p, heads, ws, s)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, s)) != hipSuccess) return hip_fail(e, "csr");
+  return ASA_OK;
+}
+
+asa_status asa_static_mask(const asa_shape* shape, const asa_head_pattern* patterns,
+                           const asa_csr* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_last_error[0] = '\0';
+  asa_status st = check_shape(shape, true);
+  if (st != ASA_OK) return st;
+  if (!patterns) return fail(ASA_ERR_NULL_ARG, "patterns is NULL (required for the static call)");
+  asa::HeadTable heads;
+  if ((st = fill_heads(shape, patterns, false, &heads)) != ASA_OK) return st;
+  if ((st = check_csr_out(shape, out)) != ASA_OK) return st;
+  const asa::MaskGeom g = geom_of(shape);
+  const size_t need = asa::mask_workspace_layout(g, false, nullptr, nullptr);
+  if ((st = check_workspace(workspace, workspace_bytes, need)) != ASA_OK) return st;
+  asa::MaskWorkspace ws;
+  asa::mask_workspace_layout(g, false, &ws, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = asa::launch_static_rows(g, heads, ws, s)) != hipSuccess) return hip_fail(e, "static rows");
+  if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, s)) != hipSuccess) return hip_fail(e, "csr");
+  return ASA_OK;
+}
+
+asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* O, int32_t o_dtype,
+                             const asa_shape* shape, const asa_csr* csr,
+                             const asa_head_pattern* patterns, float scale, void* stream) {
+  g_last_error[0] = '\0';
+  asa_status st = check_shape(shape, false);
+  if (st != ASA_OK) return st;
+  if (!Q || !K || !V || !O) return fail(ASA_ERR_NULL_ARG, "Q, K, V or O is NULL");
+  if (o_dtype != ASA_F32 && o_dtype != ASA_BF16)
+    return fail(ASA_ERR_BAD_DTYPE, "o_dtype=%d is not ASA_F32 or ASA_BF16", o_dtype);
+  if (!csr) return fail(ASA_ERR_NULL_ARG, "csr is NULL");
+  if (!csr->row_ptr || !csr->col_idx) return fail(ASA_ERR_NULL_ARG, "csr row_ptr/col_idx is NULL");
+  if (!(std::isfinite(scale))) return fail(ASA_ERR_BAD_PARAM, "scale must be finite");
+  asa::HeadTable heads;
+  if ((st = fill_heads(shape, patterns, true, &heads)) != ASA_OK) return st;
+
+  asa::AttnArgs a{};
+  a.q = Q; a.k = K; a.v = V; a.o = O;
+  a.row_ptr = csr->row_ptr;
+  a.col_idx = csr->col_idx;
+  a.B = shape->B; a.H = shape->H; a.N = shape->N; a.d = shape->d; a.blk = shape->blk;
+  a.Nb = (int)num_blocks(shape);
+  a.in_bf16 = shape->in_dtype == ASA_BF16;
+  a.out_bf16 = o_dtype == ASA_BF16;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)shape->d);
+  a.scale_log2 = (float)(sc * 1.4426950408889634);   // log2(e)
+  if (patterns)
+    for (int h = 0; h < shape->H; ++h)
+      if (patterns[h].id == ASA_PAT_SKIP) a.skip_bits[h >> 5] |= 1u << (h & 31);
+  hipError_t e = asa::launch_attention(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention");
+  return ASA_OK;
+}
+
+}  // extern "C"

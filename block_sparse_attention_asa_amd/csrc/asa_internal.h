@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI host layer and the gfx950 kernels.
+// Nothing here is exported from the shared library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace asa {
+
+constexpr int kMaxHeads = 256;       // per-head pattern table travels as a kernel argument
+constexpr int kMaxMaskBlocks = 1024; // row bitmask (32 words) and LDS sort width
+
+// Per-head pattern table passed by value (2 KiB of kernel arguments).
+struct HeadTable {
+  int32_t id[kMaxHeads];
+  int32_t param[kMaxHeads];
+};
+
+struct MaskGeom {
+  int32_t B, H, N, d, blk, Nb, words;  // words = ceil(Nb / 32) bitmask words per row
+};
+
+struct AdaptiveParams {
+  int32_t mode, k, k_cap, n_text_blocks, keep_diag;
+  double tau;
+};
+
+// Workspace carve-up for the mask builders (all offsets 256-byte aligned).
+struct MaskWorkspace {
+  double* qp;      // [B*H*Nb*d]  pooled queries, row-major
+  double* kpt;     // [B*H*d*Nb]  pooled keys, transposed per head
+  double* score;   // [B*H*Nb*Nb] block scores
+  uint32_t* bits;  // [B*H*Nb*words] kept-block bitmask per row
+  int32_t* count;  // [B*H*Nb] kept blocks per row
+};
+
+size_t mask_workspace_layout(const MaskGeom& g, bool adaptive, MaskWorkspace* ws, void* base);
+
+// Mask pipeline stages (enqueue only; return the launch status).
+hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& g,
+                       const MaskWorkspace& ws, hipStream_t s);
+hipError_t launch_scores(const MaskGeom& g, const MaskWorkspace& ws, hipStream_t s);
+hipError_t launch_select(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
+                         const MaskWorkspace& ws, hipStream_t s);
+hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const MaskWorkspace& ws,
+                              hipStream_t s);
+hipError_t launch_csr(const MaskGeom& g, const MaskWorkspace& ws, int32_t* row_ptr,
+                      int32_t* col_idx, hipStream_t s);
+
+// Attention forward.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  int32_t B, H, N, d, blk, Nb;
+  bool in_bf16, out_bf16;
+  float scale_log2;      // softmax scale times log2(e)
+  uint32_t skip_bits[kMaxHeads / 32];   // heads whose output is zero
+};
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace asa

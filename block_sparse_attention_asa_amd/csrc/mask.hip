@@ -1,0 +1,458 @@
+// Block-mask construction for content-aware block-sparse attention (gfx950).
+//
+// Adaptive source: BLADE ("BLADE: Block-Sparse Attention Meets Step Distillation for
+// Efficient Video Generation", abstract) generates a content-aware block mask per
+// input; its rule is not on the pages, so the rule here is the one stated in asa.h:
+// mean-pooled Q and K per block, float64 block scores / sqrt(d), row softmax, rank by
+// probability (ties to the smaller block), keep top-k or the shortest prefix reaching
+// the mass tau (capped), plus the diagonal and text blocks.
+// Static sources: Sparse-vDiT ("Sparse-vDiT: Sparse Attention Acceleration for Video
+// Diffusion Transformers"), "四种注意力模式" table (full, skip, diagonal,
+// multi-diagonal, vertical stripe).
+//
+// Pipeline (all on the caller's stream):
+//   pool_kernel      Q, K -> Qp [B,H,Nb,d], KpT [B,H,d,Nb] (float64 means); HBM-bound.
+//   score_kernel     S = Qp KpT / sqrt(d), 16 query blocks per workgroup so each
+//                    pooled-key panel is read once per 16 rows.
+//   select_kernel    one workgroup per row: softmax, bitonic sort of (P, c) in LDS,
+//                    prefix selection, union with forced / static blocks -> bitmask.
+//   static_kernel    one wavefront per row: static pattern bitmask only.
+//   csr_scan_kernel  exclusive scan of per-row counts -> row_ptr.
+//   csr_fill_kernel  one wavefront per row: bitmask -> ascending col_idx.
+#include <hip/hip_runtime.h>
+
+#include "asa_internal.h"
+
+namespace asa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kScoreRows = 16;   // query blocks per score workgroup
+
+__device__ inline double bf16_to_f64(uint16_t x) {
+  return (double)__uint_as_float(((uint32_t)x) << 16);
+}
+
+// ------------------------------------------------------------------ static patterns
+__device__ inline long long floor_div(long long a, long long b) {  // b > 0
+  long long q = a / b;
+  if ((a % b != 0) && (a < 0)) --q;
+  return q;
+}
+
+// Is key block c kept in query-block row r by static pattern (id, param)?
+__device__ inline bool static_keep(int id, int param, int r, int c, int N, int blk, int Nb) {
+  switch (id) {
+    case 1:  // full
+      return true;
+    case 3:  // diagonal
+      return c == r;
+    case 5:  // vertical stripe: leading `param` key blocks
+      return c < param;
+    case 4: {  // multi-diagonal, stride `param` tokens
+      const long long qlo = (long long)r * blk;
+      const long long qhi = min(qlo + blk, (long long)N) - 1;
+      const long long klo = (long long)c * blk;
+      const long long khi = min(klo + blk, (long long)N) - 1;
+      const long long lo = klo - qhi, hi = khi - qlo;   // range of j - i over the tile
+      const long long S = param;
+      return floor_div(hi, S) * S >= lo;                // a multiple of S lies in [lo, hi]
+    }
+    default:  // skip, adaptive
+      return false;
+  }
+}
+
+// ------------------------------------------------------------------ pooling
+// grid = (B*H*Nb, 2): y = 0 pools Q into Qp (row-major), y = 1 pools K into KpT.
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__ q,
+                                                        const void* __restrict__ k,
+                                                        double* __restrict__ qp,
+                                                        double* __restrict__ kpt, int N,
+                                                        int blk, int Nb) {
+  constexpr int VEC = 8;
+  constexpr int TPR = D / VEC;          // threads per token row
+  constexpr int RPP = kThreads / TPR;   // token rows per pass
+  __shared__ double red[kThreads][VEC + 1];
+
+  const int row = blockIdx.x;
+  const int bh = row / Nb, r = row - bh * Nb;
+  const int lo = r * blk, n = min(blk, N - lo);
+  const int t = threadIdx.x, col = (t % TPR) * VEC, sub = t / TPR;
+  const size_t head_off = (size_t)bh * N * D;
+
+  double acc[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) acc[j] = 0.0;
+
+  if (BF16) {
+    const uint16_t* x = static_cast<const uint16_t*>(blockIdx.y == 0 ? q : k) + head_off;
+    for (int i = sub; i < n; i += RPP) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)(lo + i) * D + col);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += bf16_to_f64((uint16_t)(w[j] & 0xffffu));
+        acc[2 * j + 1] += bf16_to_f64((uint16_t)(w[j] >> 16));
+      }
+    }
+  } else {
+    const float* x = static_cast<const float*>(blockIdx.y == 0 ? q : k) + head_off;
+    for (int i = sub; i < n; i += RPP) {
+      const float4 a = *reinterpret_cast<const float4*>(x + (size_t)(lo + i) * D + col);
+      const float4 b = *reinterpret_cast<const float4*>(x + (size_t)(lo + i) * D + col + 4);
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) red[t][j] = acc[j];
+  __syncthreads();
+  for (int s = RPP / 2; s > 0; s >>= 1) {   // fixed-order tree: deterministic
+    if (sub < s) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) red[t][j] += red[t + s * TPR][j];
+    }
+    __syncthreads();
+  }
+  if (sub == 0) {
+    const double inv_n = (double)n;
+    if (blockIdx.y == 0) {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) qp[(size_t)row * D + col + j] = red[t][j] / inv_n;
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) kpt[((size_t)bh * D + col + j) * Nb + r] = red[t][j] / inv_n;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ block scores
+// grid = B*H*ceil(Nb/16); each workgroup scores 16 query blocks against all key blocks.
+template <int D>
+__global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qp,
+                                                         const double* __restrict__ kpt,
+                                                         double* __restrict__ score, int Nb) {
+  __shared__ double qs[kScoreRows][D];
+  const int groups = (Nb + kScoreRows - 1) / kScoreRows;
+  const int bh = blockIdx.x / groups;
+  const int r0 = (blockIdx.x - bh * groups) * kScoreRows;
+  const int nr = min(kScoreRows, Nb - r0);
+  for (int i = threadIdx.x; i < kScoreRows * D; i += kThreads) {
+    const int rr = i / D, j = i - rr * D;
+    qs[rr][j] = rr < nr ? qp[((size_t)bh * Nb + r0 + rr) * D + j] : 0.0;
+  }
+  __syncthreads();
+  const double* kt = kpt + (size_t)bh * D * Nb;
+  const double sqrt_d = sqrt((double)D);
+  for (int c = threadIdx.x; c < Nb; c += kThreads) {
+    double acc[kScoreRows];
+#pragma unroll
+    for (int rr = 0; rr < kScoreRows; ++rr) acc[rr] = 0.0;
+    for (int j = 0; j < D; ++j) {
+      const double kv = kt[(size_t)j * Nb + c];
+#pragma unroll
+      for (int rr = 0; rr < kScoreRows; ++rr) acc[rr] = fma(qs[rr][j], kv, acc[rr]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < kScoreRows; ++rr)
+      if (rr < nr) score[((size_t)bh * Nb + r0 + rr) * Nb + c] = acc[rr] / sqrt_d;
+  }
+}
+
+// ------------------------------------------------------------------ block reductions
+__device__ inline double block_reduce_max(double v, double* scratch) {
+  scratch[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) scratch[threadIdx.x] = fmax(scratch[threadIdx.x], scratch[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const double r = scratch[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ inline double block_reduce_sum(double v, double* scratch) {
+  scratch[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) scratch[threadIdx.x] += scratch[threadIdx.x + s];
+    __syncthreads();
+  }
+  const double r = scratch[0];
+  __syncthreads();
+  return r;
+}
+
+// (p, c) comes before (q, e) in rank order: larger probability first, then smaller block.
+__device__ inline bool ranks_before(double p, int c, double q, int e) {
+  return p > q || (p == q && c < e);
+}
+
+// ------------------------------------------------------------------ selection
+// grid = B*H*Nb rows; one workgroup per row.
+__global__ __launch_bounds__(kThreads) void select_kernel(const double* __restrict__ score,
+                                                          uint32_t* __restrict__ bits,
+                                                          int32_t* __restrict__ count,
+                                                          MaskGeom g, AdaptiveParams p,
+                                                          HeadTable heads) {
+  __shared__ double key[kMaxMaskBlocks];
+  __shared__ int idx[kMaxMaskBlocks];
+  __shared__ double scratch[kThreads];
+  __shared__ uint32_t word[kMaxMaskBlocks / 32];
+  __shared__ int kept_prefix;
+
+  const int row = blockIdx.x;
+  const int bh = row / g.Nb, r = row - bh * g.Nb, h = bh % g.H;
+  const int tid = threadIdx.x;
+  const int pid = heads.id[h], prm = heads.param[h];
+  const int Nb = g.Nb;
+
+  if (tid < g.words) word[tid] = 0u;
+  __syncthreads();
+
+  if (pid == 2) {   // skip head: empty row
+    if (tid < g.words) bits[(size_t)row * g.words + tid] = 0u;
+    if (tid == 0) count[row] = 0;
+    return;
+  }
+  if (r < p.n_text_blocks) {   // query block holding text tokens: full row
+    for (int c = tid; c < Nb; c += kThreads) atomicOr(&word[c >> 5], 1u << (c & 31));
+  } else {
+    // softmax over all key blocks of this row
+    const double* srow = score + (size_t)row * Nb;
+    double mx = -INFINITY;
+    for (int c = tid; c < Nb; c += kThreads) mx = fmax(mx, srow[c]);
+    mx = block_reduce_max(mx, scratch);
+    double part = 0.0;
+    for (int c = tid; c < Nb; c += kThreads) {
+      const double e = exp(srow[c] - mx);
+      key[c] = e;
+      part += e;
+    }
+    const double z = block_reduce_sum(part, scratch);   // also a barrier for key[]
+    int np2 = 1;
+    while (np2 < Nb) np2 <<= 1;
+    for (int c = tid; c < np2; c += kThreads) {
+      if (c < Nb) {
+        key[c] = key[c] / z;
+        idx[c] = c;
+      } else {
+        key[c] = -1.0;           // padding ranks after every real block
+        idx[c] = 0x7fffffff;
+      }
+    }
+    __syncthreads();
+    // bitonic sort into rank order
+    for (int kk = 2; kk <= np2; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < np2; i += kThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const double a = key[i], b = key[ixj];
+            const int ia = idx[i], ib = idx[ixj];
+            const bool a_first = ranks_before(a, ia, b, ib);
+            const bool want_a_first = (i & kk) == 0;
+            if (a_first != want_a_first) {
+              key[i] = b; key[ixj] = a;
+              idx[i] = ib; idx[ixj] = ia;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // length of the adaptive prefix
+    if (tid == 0) {
+      int m;
+      if (p.mode == 0) {
+        m = min(max(p.k, 0), Nb);
+      } else {
+        m = Nb;
+        double mass = 0.0;
+        for (int t = 0; t < Nb; ++t) {   // sequential running sum in rank order
+          mass += key[t];
+          if (mass >= p.tau) { m = t + 1; break; }
+        }
+        if (p.k_cap > 0) m = min(m, p.k_cap);
+      }
+      kept_prefix = m;
+    }
+    __syncthreads();
+    const int m = kept_prefix;
+    for (int t = tid; t < m; t += kThreads) {
+      const int c = idx[t];
+      atomicOr(&word[c >> 5], 1u << (c & 31));
+    }
+    for (int c = tid; c < Nb; c += kThreads) {
+      const bool forced = (p.keep_diag && c == r) || (c < p.n_text_blocks) ||
+                          static_keep(pid, prm, r, c, g.N, g.blk, Nb);
+      if (forced) atomicOr(&word[c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  if (tid < g.words) bits[(size_t)row * g.words + tid] = word[tid];
+  if (tid < 64) {
+    int pc = tid < g.words ? __popc(word[tid]) : 0;
+    for (int off = 32; off > 0; off >>= 1) pc += __shfl_xor(pc, off, 64);
+    if (tid == 0) count[row] = pc;
+  }
+}
+
+// ------------------------------------------------------------------ static-only rows
+// One wavefront per row, 4 rows per workgroup.
+__global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__ bits,
+                                                          int32_t* __restrict__ count,
+                                                          MaskGeom g, HeadTable heads, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int bh = row / g.Nb, r = row - bh * g.Nb, h = bh % g.H;
+  const int pid = heads.id[h], prm = heads.param[h];
+  uint32_t w = 0u;
+  if (lane < g.words) {
+    for (int b = 0; b < 32; ++b) {
+      const int c = lane * 32 + b;
+      if (c < g.Nb && static_keep(pid, prm, r, c, g.N, g.blk, g.Nb)) w |= 1u << b;
+    }
+    bits[(size_t)row * g.words + lane] = w;
+  }
+  int pc = __popc(w);
+  for (int off = 32; off > 0; off >>= 1) pc += __shfl_xor(pc, off, 64);
+  if (lane == 0) count[row] = pc;
+}
+
+// ------------------------------------------------------------------ CSR
+constexpr int kScanThreads = 1024;
+
+// Single workgroup: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].
+__global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* __restrict__ count,
+                                                                int32_t* __restrict__ row_ptr,
+                                                                int rows) {
+  __shared__ int buf[kScanThreads];
+  __shared__ int carry;
+  if (threadIdx.x == 0) { carry = 0; row_ptr[0] = 0; }
+  __syncthreads();
+  for (int base = 0; base < rows; base += kScanThreads) {
+    const int i = base + threadIdx.x;
+    int v = i < rows ? count[i] : 0;
+    buf[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele scan
+      const int add = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (i < rows) row_ptr[i + 1] = carry + buf[threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x == kScanThreads - 1) carry += buf[threadIdx.x];
+    __syncthreads();
+  }
+}
+
+// One wavefront per row: kept bits -> ascending block indices.
+__global__ __launch_bounds__(kThreads) void csr_fill_kernel(const uint32_t* __restrict__ bits,
+                                                            const int32_t* __restrict__ row_ptr,
+                                                            int32_t* __restrict__ col_idx,
+                                                            int words, int rows) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  uint32_t w = lane < words ? bits[(size_t)row * words + lane] : 0u;
+  const int pc = __popc(w);
+  int incl = pc;   // inclusive prefix over lanes
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  int out = row_ptr[row] + incl - pc;
+  while (w) {
+    const int b = __ffs(w) - 1;
+    col_idx[out++] = lane * 32 + b;
+    w &= w - 1u;
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ host launchers
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t mask_workspace_layout(const MaskGeom& g, bool adaptive, MaskWorkspace* ws, void* base) {
+  const size_t rows = (size_t)g.B * g.H * g.Nb;
+  size_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  MaskWorkspace w{};
+  if (adaptive) {
+    w.qp = static_cast<double*>(take(rows * g.d * sizeof(double)));
+    w.kpt = static_cast<double*>(take(rows * g.d * sizeof(double)));
+    w.score = static_cast<double*>(take(rows * g.Nb * sizeof(double)));
+  }
+  w.bits = static_cast<uint32_t*>(take(rows * g.words * sizeof(uint32_t)));
+  w.count = static_cast<int32_t*>(take(rows * sizeof(int32_t)));
+  if (ws) *ws = w;
+  return off;
+}
+
+hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& g,
+                       const MaskWorkspace& ws, hipStream_t s) {
+  const dim3 grid((unsigned)(g.B * g.H * g.Nb), 2);
+  if (bf16) {
+    if (g.d == 128)
+      hipLaunchKernelGGL((pool_kernel<true, 128>), grid, dim3(kThreads), 0, s, q, k, ws.qp, ws.kpt, g.N, g.blk, g.Nb);
+    else
+      hipLaunchKernelGGL((pool_kernel<true, 64>), grid, dim3(kThreads), 0, s, q, k, ws.qp, ws.kpt, g.N, g.blk, g.Nb);
+  } else {
+    if (g.d == 128)
+      hipLaunchKernelGGL((pool_kernel<false, 128>), grid, dim3(kThreads), 0, s, q, k, ws.qp, ws.kpt, g.N, g.blk, g.Nb);
+    else
+      hipLaunchKernelGGL((pool_kernel<false, 64>), grid, dim3(kThreads), 0, s, q, k, ws.qp, ws.kpt, g.N, g.blk, g.Nb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const MaskGeom& g, const MaskWorkspace& ws, hipStream_t s) {
+  const int groups = (g.Nb + kScoreRows - 1) / kScoreRows;
+  const dim3 grid((unsigned)(g.B * g.H * groups));
+  if (g.d == 128)
+    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kThreads), 0, s, ws.qp, ws.kpt, ws.score, g.Nb);
+  else
+    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kThreads), 0, s, ws.qp, ws.kpt, ws.score, g.Nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
+                         const MaskWorkspace& ws, hipStream_t s) {
+  const dim3 grid((unsigned)(g.B * g.H * g.Nb));
+  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, s, ws.score, ws.bits, ws.count, g, p, heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const MaskWorkspace& ws,
+                              hipStream_t s) {
+  const int rows = g.B * g.H * g.Nb;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  hipLaunchKernelGGL(static_kernel, grid, dim3(kThreads), 0, s, ws.bits, ws.count, g, heads, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_csr(const MaskGeom& g, const MaskWorkspace& ws, int32_t* row_ptr,
+                      int32_t* col_idx, hipStream_t s) {
+  const int rows = g.B * g.H * g.Nb;
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws.count, row_ptr, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, ws.bits,
+                     row_ptr, col_idx, g.words, rows);
+  return hipGetLastError();
+}
+
+}  // namespace asa

@@ -1,0 +1,190 @@
+/*
+ * asa.h -- C ABI of the MI355X (gfx950) content-aware block-sparse attention library.
+ *
+ * The library builds block masks over (query-block, key-block) tiles and computes
+ * softmax(Q K^T / sqrt(d)) V over the kept tiles only.
+ *
+ * Sources of the operations (page title, then section / formula / table):
+ *  - "Sparse-vDiT: Sparse Attention Acceleration for Video Diffusion Transformers",
+ *    section 三 "核心公式": full attention per head softmax(Q_h K_h^T / sqrt(d)) V_h of
+ *    shape B x N x d, and the masked form Attention(Q, K, V, M).
+ *  - same page, "四种注意力模式" table: the static mask sources M0 full, M1 skip (output
+ *    set to zero), M2 diagonal, M3 multi-diagonal, M4 vertical stripe.
+ *  - "BLADE: Block-Sparse Attention Meets Step Distillation for Efficient Video
+ *    Generation", abstract: Adaptive Block-Sparse Attention (ASA) generates a
+ *    content-aware sparsity mask from the input.  The pages leave ASA's rule open; the
+ *    rule implemented here is stated at asa_build_mask below.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are contiguous row-major [B, H, N, d] device arrays.  d is 64 or 128; the
+ *    block size blk (used for both query and key blocks, so the diagonal is defined) is
+ *    64 or 128.  Nb = ceil(N / blk); block r covers tokens [r*blk, min((r+1)*blk, N)).
+ *  - Every pointer argument that names tensor data is a DEVICE pointer.  Struct
+ *    arguments (asa_shape, asa_adaptive, asa_head_pattern arrays, asa_csr) are HOST
+ *    memory read during the call only.
+ *  - Ownership: the caller allocates every buffer (outputs and workspace).  The library
+ *    allocates nothing, keeps no state between calls and never synchronizes: all work is
+ *    enqueued on `stream` (a hipStream_t; NULL means the default stream).
+ *  - Errors: arguments are validated on the host before anything is enqueued; an invalid
+ *    call returns a negative asa_status, enqueues nothing, and asa_last_error() returns a
+ *    thread-local message.  Launch failures return ASA_ERR_HIP.  Faults inside kernels
+ *    surface at the caller's next synchronization.  No C++ exception crosses the ABI.
+ *  - Determinism: identical inputs give bit-identical CSR arrays and outputs.
+ */
+#ifndef ASA_H_
+#define ASA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum asa_status {
+  ASA_OK = 0,
+  ASA_ERR_NULL_ARG = -1,     /* a required pointer is NULL                         */
+  ASA_ERR_BAD_SHAPE = -2,    /* B, H, N <= 0, or sizes overflow int32 indexing      */
+  ASA_ERR_BAD_DTYPE = -3,    /* dtype code not ASA_F32 / ASA_BF16                   */
+  ASA_ERR_UNSUPPORTED = -4,  /* d not in {64,128}, blk not in {64,128}, Nb > 1024    */
+  ASA_ERR_CAPACITY = -5,     /* csr->capacity below asa_csr_capacity()              */
+  ASA_ERR_WORKSPACE = -6,    /* workspace NULL or smaller than the *_workspace_size  */
+  ASA_ERR_BAD_PATTERN = -7,  /* unknown pattern id or invalid pattern parameter      */
+  ASA_ERR_BAD_PARAM = -8,    /* adaptive parameters out of range                     */
+  ASA_ERR_HIP = -9           /* a HIP runtime call or kernel launch failed           */
+} asa_status;
+
+typedef enum asa_dtype { ASA_F32 = 0, ASA_BF16 = 1 } asa_dtype;
+
+/* Per-head mask sources.  Codes follow the Sparse-vDiT mode table (M0..M4) plus the
+ * adaptive ASA source. */
+enum {
+  ASA_PAT_ADAPTIVE = 0,   /* adaptive only (asa_build_mask)                                 */
+  ASA_PAT_FULL = 1,       /* M0: every key block                                           */
+  ASA_PAT_SKIP = 2,       /* M1: no key block; the head's output is zero                   */
+  ASA_PAT_DIAG = 3,       /* M2: key block c == query block r                              */
+  ASA_PAT_MULTIDIAG = 4,  /* M3: param = stride S in tokens (> 0); tile (r,c) kept iff some
+                             query i in block r and key j in block c have (j - i) % S == 0  */
+  ASA_PAT_VSTRIPE = 5     /* M4: param = s >= 0 leading key blocks (global tokens), c < s   */
+};
+
+enum { ASA_MODE_TOPK = 0, ASA_MODE_TAU = 1 };
+
+typedef struct asa_shape {
+  int32_t B, H, N, d, blk;
+  int32_t in_dtype;        /* asa_dtype of Q, K, V */
+} asa_shape;
+
+typedef struct asa_adaptive {
+  int32_t mode;            /* ASA_MODE_TOPK or ASA_MODE_TAU                                  */
+  int32_t k;               /* TOPK: number of key blocks kept per row (>= 0)                 */
+  double tau;              /* TAU: cumulative probability mass to reach, in [0, +inf)        */
+  int32_t k_cap;           /* TAU: cap on the adaptive prefix length (0 = no cap)            */
+  int32_t n_text;          /* leading text tokens: blocks holding any are kept as rows and
+                              columns (0 = none)                                             */
+  int32_t keep_diag;       /* 1 = always keep the diagonal block                             */
+} asa_adaptive;
+
+typedef struct asa_head_pattern {
+  int32_t id;              /* ASA_PAT_* */
+  int32_t param;           /* stride in tokens (MULTIDIAG) or leading blocks (VSTRIPE) */
+} asa_head_pattern;
+
+/* Block mask in CSR form: one row per (b, h, query block r), rows in [B, H, Nb] order.
+ * row_ptr has B*H*Nb + 1 entries (row_ptr[0] = 0, row_ptr[last] = number of kept tiles);
+ * col_idx lists the kept key blocks of each row in ascending order.  Both are device
+ * int32 arrays owned by the caller; capacity is the length of col_idx in elements. */
+typedef struct asa_csr {
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  int64_t capacity;
+} asa_csr;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t asa_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* asa_status_string(asa_status status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* asa_last_error(void);
+
+/* Number of col_idx elements the mask builders require: B*H*Nb*Nb (the worst case, since
+ * the kept count is known only on the device).  Returns -1 for an invalid shape. */
+int64_t asa_csr_capacity(const asa_shape* shape);
+
+/* Workspace bytes for asa_build_mask (pooled Q and K, block scores, row bitmasks and
+ * counts).  Returns 0 for an invalid shape. */
+size_t asa_build_mask_workspace_size(const asa_shape* shape);
+
+/* Workspace bytes for asa_static_mask (row bitmasks and counts).  0 for an invalid shape. */
+size_t asa_static_mask_workspace_size(const asa_shape* shape);
+
+/*
+ * asa_build_mask -- adaptive (ASA) block mask, unioned with forced and static blocks.
+ *
+ * Source: BLADE abstract (content-aware adaptive block mask, rule left open by the pages)
+ * and the Sparse-vDiT mode table (static sources).  The rule computed, in float64:
+ *   1. Qp[r] = mean of Q over the tokens of block r; Kp[c] likewise (a partial last block
+ *      is averaged over its own tokens).
+ *   2. S[r,c] = Qp[r] . Kp[c] / sqrt(d).
+ *   3. P[r,:] = softmax of S[r,:] over all Nb key blocks.
+ *   4. Order the key blocks by P descending, ties by smaller index.
+ *   5. Adaptive set A_r: TOPK keeps the first min(k, Nb); TAU keeps the shortest prefix
+ *      whose running sum (in rank order) is >= tau (all Nb if none), then at most k_cap.
+ *   6. kept_r = A_r, plus block r if keep_diag, plus every key block holding a text token;
+ *      a query block holding a text token keeps every key block.
+ *   7. Heads whose pattern id is not ASA_PAT_ADAPTIVE add their static pattern's blocks;
+ *      an ASA_PAT_SKIP head gets empty rows.
+ *
+ * Q, K       device [B,H,N,d] of shape->in_dtype.
+ * adaptive   host struct (see asa_adaptive).
+ * patterns   host array [H] or NULL (NULL = every head ASA_PAT_ADAPTIVE).
+ * out        host struct with device row_ptr / col_idx; capacity >= asa_csr_capacity().
+ * workspace  device buffer of at least asa_build_mask_workspace_size(shape) bytes,
+ *            256-byte aligned; its contents on entry are ignored.
+ */
+asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
+                          const asa_adaptive* adaptive, const asa_head_pattern* patterns,
+                          const asa_csr* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * asa_static_mask -- block mask from per-head static patterns alone (Sparse-vDiT mode
+ * table: full, skip, diagonal, multi-diagonal, vertical stripe).  No tensor is read.
+ * Every entry of `patterns` (host array [H], required) must be a static id (not
+ * ASA_PAT_ADAPTIVE).  shape->d and shape->in_dtype are not used by this call but must be
+ * valid.  Workspace: asa_static_mask_workspace_size(shape) bytes, 256-byte aligned.
+ */
+asa_status asa_static_mask(const asa_shape* shape, const asa_head_pattern* patterns,
+                           const asa_csr* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * asa_attention_fwd -- block-sparse attention forward over the kept tiles.
+ *
+ * Source: Sparse-vDiT section 三 "核心公式" (attention formula and masked attention M).
+ * For each query token i of block r: O_i = sum_j softmax_j(Q_i . K_j * scale) V_j over
+ * the tokens j of the key blocks listed in CSR row (b,h,r); O_i = 0 when the row is empty
+ * or the head's pattern is ASA_PAT_SKIP.  No token-level masking inside kept tiles.
+ *
+ * Q, K, V    device [B,H,N,d] of shape->in_dtype.  For ASA_BF16 inputs the products run
+ *            on bf16 matrix cores with fp32 accumulation (softmax weights are rounded to
+ *            bf16 before the PV product, and the normalizer sums those rounded weights);
+ *            ASA_F32 inputs run entirely in fp32.
+ * O          device [B,H,N,d] of o_dtype (ASA_F32 recommended; ASA_BF16 rounds to bf16).
+ * csr        host struct with device arrays, e.g. from asa_build_mask / asa_static_mask;
+ *            col_idx entries must lie in [0, Nb) (not checked on the device).
+ * patterns   host array [H] or NULL; used only to zero ASA_PAT_SKIP heads without
+ *            reading their CSR rows.
+ * scale      softmax scale; <= 0 selects 1/sqrt(d).
+ */
+asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* O,
+                             int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
+                             const asa_head_pattern* patterns, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ASA_H_ */

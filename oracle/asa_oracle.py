@@ -298,6 +298,18 @@ def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray, blk: i
     return O
 
 
+def attention_block(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray, blk: int,
+                    b: int, h: int, r: int) -> np.ndarray:
+    """Outputs of the query tokens of block r of head (b, h): [n_r, d]."""
+    N, d = Q.shape[2], Q.shape[3]
+    lo, hi = block_range(r, N, blk)
+    J = kept_tokens(M[b, h, r], N, blk)
+    if J.size == 0:
+        return np.zeros((hi - lo, d), dtype=np.float64)
+    return _row_attention(Q[b, h, lo:hi].astype(np.float64), K[b, h, J].astype(np.float64),
+                          V[b, h, J].astype(np.float64))
+
+
 def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray, blk: int,
                    rows: Sequence[Tuple[int, int, int]]) -> np.ndarray:
     """Outputs for selected query tokens (b, h, i) only: [len(rows), d]."""

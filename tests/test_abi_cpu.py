@@ -1,0 +1,137 @@
+"""C-ABI library: loads, exports every declared symbol, validates arguments (no GPU needed).
+
+Every call here fails validation on the host before anything is enqueued, so no
+kernel runs and no device memory is touched (the fake addresses are never used).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_asa_amd as asa
+from block_sparse_attention_asa_amd import asa_shape, asa_adaptive, asa_head_pattern, asa_csr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "asa.h")
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+OK, NULL_ARG, BAD_SHAPE, BAD_DTYPE, UNSUPPORTED, CAPACITY, WORKSPACE, BAD_PATTERN, BAD_PARAM = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(asa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("asa_build_mask", "asa_static_mask", "asa_attention_fwd"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", asa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"declared in asa.h but not exported: {missing}"
+    assert set(asa.EXPORTS) == set(declared_functions())
+
+
+def _shape(B=1, H=2, N=1024, d=64, blk=64, dt=asa.ASA_BF16):
+    return asa_shape(B, H, N, d, blk, dt)
+
+
+def _csr(cap):
+    return asa_csr(0x20000, 0x30000, cap)
+
+
+def _build(shape, ad=None, pats=None, csr=None, ws_bytes=1 << 30, q=FAKE, k=FAKE, ws=0x40000):
+    ad = ad or asa_adaptive(asa.TOPK, 4, 0.0, 0, 0, 1)
+    csr = csr or _csr(asa.lib.asa_csr_capacity(ctypes.byref(shape)))
+    return asa.lib.asa_build_mask(q, k, ctypes.byref(shape), ctypes.byref(ad), pats, ctypes.byref(csr),
+                                  ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_capacity_and_workspace_sizes():
+    s = _shape(N=1000, blk=64)                       # Nb = 16 (ragged)
+    assert asa.lib.asa_csr_capacity(ctypes.byref(s)) == 2 * 16 * 16
+    ws = asa.lib.asa_build_mask_workspace_size(ctypes.byref(s))
+    rows = 2 * 16
+    assert ws >= rows * 64 * 8 * 2 + rows * 16 * 8 + rows * 4 + rows * 4
+    assert asa.lib.asa_static_mask_workspace_size(ctypes.byref(s)) >= rows * 8
+    assert asa.lib.asa_build_mask_workspace_size(ctypes.byref(_shape(d=96))) == 0
+    assert asa.lib.asa_csr_capacity(None) == -1
+
+
+@pytest.mark.parametrize("shape,code", [
+    (_shape(B=0), BAD_SHAPE), (_shape(N=-5), BAD_SHAPE), (_shape(d=96), UNSUPPORTED),
+    (_shape(blk=32), UNSUPPORTED), (_shape(dt=7), BAD_DTYPE), (_shape(H=300), UNSUPPORTED),
+    (_shape(N=64 * 1025, blk=64), UNSUPPORTED),           # Nb > 1024 for the mask builders
+])
+def test_build_mask_rejects_shapes(shape, code):
+    assert _build(shape) == code
+    assert asa.lib.asa_last_error().decode() != ""
+
+
+def test_build_mask_rejects_arguments():
+    s = _shape()
+    assert _build(s, q=None) == NULL_ARG
+    assert _build(s, ad=asa_adaptive(5, 4, 0.0, 0, 0, 1)) == BAD_PARAM
+    assert _build(s, ad=asa_adaptive(asa.TOPK, -1, 0.0, 0, 0, 1)) == BAD_PARAM
+    assert _build(s, ad=asa_adaptive(asa.TAU, 0, float("nan"), 0, 0, 1)) == BAD_PARAM
+    assert _build(s, ad=asa_adaptive(asa.TAU, 0, 0.9, -2, 0, 1)) == BAD_PARAM
+    assert _build(s, ad=asa_adaptive(asa.TOPK, 4, 0.0, 0, 5000, 1)) == BAD_PARAM
+    assert _build(s, ad=asa_adaptive(asa.TOPK, 4, 0.0, 0, 0, 2)) == BAD_PARAM
+    assert _build(s, csr=_csr(10)) == CAPACITY
+    assert _build(s, ws_bytes=100) == WORKSPACE
+    assert _build(s, ws=0) == WORKSPACE
+    assert _build(s, ws=0x40010) == WORKSPACE                # misaligned
+    bad = (asa_head_pattern * 2)(asa_head_pattern(9, 0), asa_head_pattern(0, 0))
+    assert _build(s, pats=bad) == BAD_PATTERN
+    bad = (asa_head_pattern * 2)(asa_head_pattern(asa.MULTIDIAG, 0), asa_head_pattern(0, 0))
+    assert _build(s, pats=bad) == BAD_PATTERN
+    bad = (asa_head_pattern * 2)(asa_head_pattern(asa.VSTRIPE, -1), asa_head_pattern(0, 0))
+    assert _build(s, pats=bad) == BAD_PATTERN
+
+
+def test_static_mask_rejects_arguments():
+    s = _shape()
+    cap = asa.lib.asa_csr_capacity(ctypes.byref(s))
+    csr = _csr(cap)
+    good = (asa_head_pattern * 2)(asa_head_pattern(asa.DIAG, 0), asa_head_pattern(asa.FULL, 0))
+    adaptive = (asa_head_pattern * 2)(asa_head_pattern(asa.ADAPTIVE, 0), asa_head_pattern(asa.FULL, 0))
+    call = asa.lib.asa_static_mask
+    assert call(ctypes.byref(s), None, ctypes.byref(csr), ctypes.c_void_p(0x40000), 1 << 30, None) == NULL_ARG
+    assert call(ctypes.byref(s), adaptive, ctypes.byref(csr), ctypes.c_void_p(0x40000), 1 << 30, None) == BAD_PATTERN
+    small = _csr(cap - 1)
+    assert call(ctypes.byref(s), good, ctypes.byref(small), ctypes.c_void_p(0x40000), 1 << 30, None) == CAPACITY
+    assert call(ctypes.byref(s), good, ctypes.byref(csr), ctypes.c_void_p(0x40000), 8, None) == WORKSPACE
+    nullcsr = asa_csr(0, 0x30000, cap)
+    assert call(ctypes.byref(s), good, ctypes.byref(nullcsr), ctypes.c_void_p(0x40000), 1 << 30, None) == NULL_ARG
+
+
+def test_attention_rejects_arguments():
+    s = _shape()
+    csr = _csr(10)
+    call = asa.lib.asa_attention_fwd
+    assert call(FAKE, FAKE, FAKE, None, asa.ASA_F32, ctypes.byref(s), ctypes.byref(csr), None, 0.0, None) == NULL_ARG
+    assert call(FAKE, FAKE, FAKE, FAKE, 5, ctypes.byref(s), ctypes.byref(csr), None, 0.0, None) == BAD_DTYPE
+    assert call(FAKE, FAKE, FAKE, FAKE, asa.ASA_F32, ctypes.byref(_shape(d=32)), ctypes.byref(csr), None, 0.0,
+                None) == UNSUPPORTED
+    assert call(FAKE, FAKE, FAKE, FAKE, asa.ASA_F32, ctypes.byref(s), None, None, 0.0, None) == NULL_ARG
+    assert call(FAKE, FAKE, FAKE, FAKE, asa.ASA_F32, ctypes.byref(s), ctypes.byref(csr), None,
+                float("inf"), None) == BAD_PARAM
+    bad = (asa_head_pattern * 2)(asa_head_pattern(42, 0), asa_head_pattern(0, 0))
+    assert call(FAKE, FAKE, FAKE, FAKE, asa.ASA_F32, ctypes.byref(s), ctypes.byref(csr), bad, 0.0,
+                None) == BAD_PATTERN
+
+
+def test_status_strings():
+    assert asa.lib.asa_status_string(0) == b"ASA_OK"
+    assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
+    assert asa.lib.asa_version() >= 10000
