@@ -71,11 +71,12 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
 }
 __device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// Position of key kk inside a transposed V row: bits 2 and 3 of the index are swapped so
-// that the 8 keys a lane half feeds to one PV k-step are contiguous (16 bytes for bf16).
-__device__ inline int vt_pos(int kk) {
-  return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
-}
+// LDS tile layout (K and V alike): row-major [BLK keys][D], no padding, 16-byte granules
+// XOR-swizzled per row.  Physical granule = logical granule ^ swz(row).  swz maps 8
+// consecutive rows to 8 distinct values (conflict-free 16-byte K-fragment reads across 8
+// lanes) and any 4 consecutive rows starting at a multiple of 4 to {2m + b} (conflict-free
+// transpose reads of 2 adjacent granules x 4 rows).
+__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 // Workgroup id -> row, keeping consecutive rows (same head) on one XCD: dispatch assigns
 // workgroup ids round-robin over the 8 XCDs, so XCD x receives ids x, x+8, ...
@@ -90,8 +91,63 @@ template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int kGran = 8; };   // elements per 16 B
 template <> struct Elem<float> { static constexpr int kGran = 4; };
 
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier without a memory fence: the caller has already waited for whatever
+// must be visible (vmcnt for LDS DMA, lgkmcnt for its own LDS traffic).  A fenced
+// __syncthreads() would also wait for LDS DMA still in flight for the next tile.
+__device__ inline void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0 << 8) | (7 << 4) | 15 | (3 << 14));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane L's 16 bytes
+// land at LDS byte address lds_base + 16 * L.  Written as an asm block so that the
+// compiler's wait insertion does not serialize it against unrelated LDS reads; the
+// instruction has no register results, and every reader of the destination waits on
+// vmcnt and a barrier first.  M0 carries the LDS base (one wait state after writing it).
+__device__ inline void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_base), "v"(gptr)
+      : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global -> LDS copy of one key block (rows >= nkv re-read row nkv-1: finite data
+// that the softmax masks out).  Each instruction of wave w writes 64 consecutive 16-byte
+// granules of the tile; lane L picks the global granule that belongs at its slot.
+template <typename T, int D, int BLK, int NT>
+__device__ inline void dma_tile(uint4* tile, const T* src, int nkv, int tid) {
+  constexpr int GPR = D * (int)sizeof(T) / 16;          // granules per row
+  constexpr int NG = BLK * GPR;                          // granules per tile
+  constexpr int G = Elem<T>::kGran;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t base = lds_addr(tile) + (uint32_t)w * 64u * 16u;
+#pragma unroll
+  for (int it = 0; it < NG / NT; ++it) {
+    const int slot = it * NT + tid;
+    const int row = slot / GPR, pg = slot - row * GPR;
+    const int lg = pg ^ swz(row);
+    const int srow = min(row, nkv - 1);
+    dma16(src + (size_t)srow * D + lg * G, base + (uint32_t)(it * NT * 16));
+  }
+}
+
 template <typename T, typename TO, int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(const T* __restrict__ Q,
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(const T* __restrict__ Q,
                                                            const T* __restrict__ K,
                                                            const T* __restrict__ V,
                                                            TO* __restrict__ O,
@@ -100,18 +156,21 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(const T* __restrict__
                                                            int H, int N, int Nb, int total_rows,
                                                            float scale_log2, AttnArgs meta) {
   constexpr int kWaves = BLK / 32;
-  constexpr int kThreadsWg = 64 * kWaves;
+  constexpr int NT = 64 * kWaves;
   constexpr int G = Elem<T>::kGran;
-  constexpr int KSTR = D + G;      // K row stride (elements): 16 bytes of padding
-  constexpr int VSTR = BLK + G;    // transposed-V row stride (elements)
+  constexpr int GPR = D * (int)sizeof(T) / 16;
+  constexpr int NG = BLK * GPR;
+  constexpr int NLD = NG / NT;     // DMA instructions per thread per tile
   constexpr int kQk = D / 16;      // k-steps of S^T = K Q^T
   constexpr int kSub = BLK / 32;   // 32-key subtiles per key block
   constexpr int kPv = BLK / 16;    // k-steps of O^T = V^T P^T
   constexpr int kOut = D / 32;     // 32-column output subtiles
   constexpr bool kBf16 = sizeof(T) == 2;
+  static_assert(NG % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(GPR >= 8, "swizzle needs at least 8 granules per row");
 
-  __shared__ __attribute__((aligned(16))) T Ks[BLK * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VSTR];
+  __shared__ uint4 Kt[NG];
+  __shared__ uint4 Vt[NG];
 
   const int row = xcd_row(blockIdx.x, total_rows);
   const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
@@ -120,7 +179,9 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(const T* __restrict__
   const size_t head = (size_t)bh * N * D;
   const int qi = r * BLK + w * 32 + qn;
 
-  int e0 = row_ptr[row], e1 = row_ptr[row + 1];
+  // CSR bounds and block indices are wave-uniform: keep them in scalar registers
+  const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[row]);
+  int e1 = __builtin_amdgcn_readfirstlane(row_ptr[row + 1]);
   if ((meta.skip_bits[h >> 5] >> (h & 31)) & 1u) e1 = e0;
 
   f32x16_t acc[kOut];
@@ -138,58 +199,58 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(const T* __restrict__
         qf[t] = Frag<T>{};
       }
     }
+    const T* vt = reinterpret_cast<const T*>(Vt);
+    // Kept block indices of this row, 64 at a time, one per lane (read back with readlane).
+    int cbase = e0;
+    int cvec = e0 + lane < e1 ? col_idx[e0 + lane] : 0;
+    // prologue: K and V of the first kept block; then drain every outstanding load so the
+    // loop below starts with only its own transfers in flight
+    int c = __builtin_amdgcn_readlane(cvec, 0);
+    {
+      const int nkv = min(BLK, N - c * BLK);
+      dma_tile<T, D, BLK, NT>(Kt, K + head + (size_t)c * BLK * D, nkv, tid);
+      dma_tile<T, D, BLK, NT>(Vt, V + head + (size_t)c * BLK * D, nkv, tid);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
     for (int e = e0; e < e1; ++e) {
-      const int c = col_idx[e];
-      const int kv0 = c * BLK;
-      const int nkv = min(BLK, N - kv0);
-      __syncthreads();   // previous tile fully consumed
-      // K tile, row-major with padding
-      for (int i = tid; i < BLK * (D / G); i += kThreadsWg) {
-        const int kr = i / (D / G), gc = i - kr * (D / G);
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (kr < nkv) val = *reinterpret_cast<const uint4*>(K + head + (size_t)(kv0 + kr) * D + gc * G);
-        *reinterpret_cast<uint4*>(Ks + kr * KSTR + gc * G) = val;
-      }
-      // V tile, transposed: item = (4-key group a, 8-column group g)
-      for (int i = tid; i < (BLK / 4) * (D / 8); i += kThreadsWg) {
-        const int a = i / (D / 8), g = i - a * (D / 8);
-        T vv[4][8];
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int kr = 4 * a + e4;
-#pragma unroll
-          for (int hh = 0; hh < 8 / G; ++hh) {
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (kr < nkv) val = *reinterpret_cast<const uint4*>(V + head + (size_t)(kv0 + kr) * D + 8 * g + hh * G);
-            *reinterpret_cast<uint4*>(&vv[e4][hh * G]) = val;
-          }
+      const int nkv = min(BLK, N - c * BLK);
+      const bool more = e + 1 < e1;
+      int cn = 0;
+      if (more) {
+        if (e + 1 - cbase == 64) {   // next batch of indices (rows longer than 64 blocks)
+          cbase += 64;
+          cvec = cbase + lane < e1 ? col_idx[cbase + lane] : 0;
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // rare: drains the tile transfers too
         }
-        const int pos = vt_pos(4 * a);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          T* dst = Vt + (8 * g + jj) * VSTR + pos;
-          if (kBf16) {
-            const uint32_t lo = (uint32_t)(uint16_t)vv[0][jj] | ((uint32_t)(uint16_t)vv[1][jj] << 16);
-            const uint32_t hi = (uint32_t)(uint16_t)vv[2][jj] | ((uint32_t)(uint16_t)vv[3][jj] << 16);
-            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-          } else {
-            *reinterpret_cast<float4*>(dst) =
-                make_float4((float)vv[0][jj], (float)vv[1][jj], (float)vv[2][jj], (float)vv[3][jj]);
-          }
-        }
+        cn = __builtin_amdgcn_readlane(cvec, e + 1 - cbase);
       }
-      __syncthreads();
+      const int nkv_n = min(BLK, N - cn * BLK);
 
+      // K(e) landed (V(e) may still be in flight)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD));
+      wg_barrier();
       // S^T = K Q^T
       f32x16_t s[kSub];
 #pragma unroll
       for (int is = 0; is < kSub; ++is) {
         s[is] = f32x16_t{};
+        const int kr = 32 * is + qn;
 #pragma unroll
-        for (int t = 0; t < kQk; ++t)
-          mma_k16(s[is], lds_frag(Ks + (32 * is + qn) * KSTR + 16 * t + 8 * hf), qf[t]);
+        for (int t = 0; t < kQk; ++t) {
+          Frag<T> a;
+          if constexpr (kBf16) {
+            a.v = Kt[kr * GPR + ((2 * t + hf) ^ swz(kr))];
+          } else {
+            a.a = *reinterpret_cast<const float4*>(&Kt[kr * GPR + ((4 * t + 2 * hf) ^ swz(kr))]);
+            a.b = *reinterpret_cast<const float4*>(&Kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz(kr))]);
+          }
+          mma_k16(s[is], a, qf[t]);
+        }
       }
+      wg_barrier();   // every wave is done with K(e)
+      if (more) dma_tile<T, D, BLK, NT>(Kt, K + head + (size_t)cn * BLK * D, nkv_n, tid);
+
       // scale (log2 domain), mask keys past N, row max
       float mx = -INFINITY;
 #pragma unroll
@@ -233,13 +294,55 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(const T* __restrict__
       l_run = l_run * alpha + lsum;
 #pragma unroll
       for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
+
+      // V(e) landed (K(e+1) may still be in flight)
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      }
+      wg_barrier();
       // O^T += V^T P^T
 #pragma unroll
       for (int io = 0; io < kOut; ++io) {
 #pragma unroll
-        for (int u = 0; u < kPv; ++u)
-          mma_k16(acc[io], lds_frag(Vt + (32 * io + qn) * VSTR + 16 * u + 8 * hf), pf[u]);
+        for (int u = 0; u < kPv; ++u) {
+          Frag<T> a;
+          if constexpr (kBf16) {
+            // transpose reads: lane s of 16-lane group g supplies row kbase + s/4, columns
+            // dbase + 4*(s%4) .. +3; lane i of the group receives column dbase + i of rows
+            // kbase .. kbase+3, i.e. V^T[d][4 consecutive keys].
+            const int g = lane >> 4, sl = lane & 15;
+            const int dcol = 32 * io + 16 * (g & 1) + 4 * (sl & 3);
+            short4_t part[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
+              const int gran = (dcol >> 3) ^ swz(kr);
+              const uint16_t* p = vt + kr * D + gran * 8 + (dcol & 7);
+              part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) short4_t*)(p));
+            }
+            const uint2 lo = __builtin_bit_cast(uint2, part[0]);
+            const uint2 hi = __builtin_bit_cast(uint2, part[1]);
+            a.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          } else {
+            const int d = 32 * io + qn;
+            float av[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int kr = 16 * u + 8 * (jj >> 2) + 4 * hf + (jj & 3);
+              av[jj] = vt[(kr * GPR + ((d / G) ^ swz(kr))) * G + (d % G)];
+            }
+            a.a = make_float4(av[0], av[1], av[2], av[3]);
+            a.b = make_float4(av[4], av[5], av[6], av[7]);
+          }
+          mma_k16(acc[io], a, pf[u]);
+        }
       }
+      wg_barrier();   // every wave is done with V(e)
+      if (more) dma_tile<T, D, BLK, NT>(Vt, V + head + (size_t)cn * BLK * D, nkv_n, tid);
+      c = cn;
     }
   }
 
