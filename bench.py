@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -218,6 +220,13 @@ def main():
         "step_ms_events": round(step_ms_ev, 4),
         **result_extra,
     }
+    if args.calib_copy > 0:
+        src = torch.ones(args.calib_copy << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline (bounded sample)")
         result["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)

@@ -22,6 +22,8 @@
 // row 8*(i/4) + 4*(l/32) + (i%4), column l%32.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "asa_internal.h"
 
 namespace asa {
@@ -29,6 +31,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Eight consecutive operand elements along the contraction (k) axis of one lane.
 template <typename T> struct Frag;
@@ -62,6 +65,14 @@ __device__ inline void mma_k16(f32x16_t& acc, const Frag<float>& a, const Frag<f
   const float bv[8] = {b.a.x, b.a.y, b.a.z, b.a.w, b.b.x, b.b.y, b.b.z, b.b.w};
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+}
+
+// max(a, b, c) in one instruction.  Written out because fmaxf on MFMA results makes the
+// compiler quiet each input first (the scores here are never NaN).
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // Round to bf16 (round to nearest even) and return both the bits and the rounded value.
@@ -107,54 +118,61 @@ __device__ inline void wg_barrier() {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane L's 16 bytes
-// land at LDS byte address lds_base + 16 * L.  Written as an asm block so that the
-// compiler's wait insertion does not serialize it against unrelated LDS reads; the
-// instruction has no register results, and every reader of the destination waits on
-// vmcnt and a barrier first.  M0 carries the LDS base (one wait state after writing it).
-__device__ inline void dma16(const void* gptr, uint32_t lds_base) {
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane L reads
+// 16 bytes at gbase + voff and they land at LDS byte address lds_base + 16 * L.  Written as
+// an asm block so that the compiler's wait insertion does not serialize it against
+// unrelated LDS reads; the instruction has no register results, and every reader of the
+// destination waits on vmcnt and a barrier first.  M0 carries the LDS base (one wait state
+// after writing it).
+template <int kLdsOff>
+__device__ inline void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  const uint64_t g = reinterpret_cast<uint64_t>(gbase);
+  // readfirstlane returns int: go through uint32_t so the low half is zero-extended
+  const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(g >> 32));
+  const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)g);
+  const uint64_t gu = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
+      "s_add_u32 m0, %0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
+      "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds_base), "v"(gptr)
-      : "memory", "m0");
+      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(gu), "i"(kLdsOff)
+      : "memory");
 }
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Direct global -> LDS copy of one key block (rows >= nkv re-read row nkv-1: finite data
-// that the softmax masks out).  Each instruction of wave w writes 64 consecutive 16-byte
-// granules of the tile; lane L picks the global granule that belongs at its slot.
-template <typename T, int D, int BLK, int NT>
-__device__ inline void dma_tile(uint4* tile, const T* src, int nkv, int tid) {
-  constexpr int GPR = D * (int)sizeof(T) / 16;          // granules per row
-  constexpr int NG = BLK * GPR;                          // granules per tile
-  constexpr int G = Elem<T>::kGran;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t base = lds_addr(tile) + (uint32_t)w * 64u * 16u;
-#pragma unroll
-  for (int it = 0; it < NG / NT; ++it) {
-    const int slot = it * NT + tid;
-    const int row = slot / GPR, pg = slot - row * GPR;
-    const int lg = pg ^ swz(row);
-    const int srow = min(row, nkv - 1);
-    dma16(src + (size_t)srow * D + lg * G, base + (uint32_t)(it * NT * 16));
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. n-1.
+template <int I, int N_, typename F>
+__device__ inline void static_for_impl(F&& f) {
+  if constexpr (I < N_) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N_>(f);
   }
+}
+template <int N_, typename F>
+__device__ inline void static_for(F&& f) { static_for_impl<0, N_>(f); }
+
+// Per-thread byte offsets (within one key block) of the 16-byte granules this thread
+// transfers: instruction `it` of wave w fills LDS granule slots it*NT + 64*w + lane, which
+// hold logical granule (slot % GPR) ^ swz(row) of row slot / GPR.  Rows at or past nkv
+// re-read row nkv-1 (finite data that the softmax masks out).
+template <typename T, int D, int BLK, int NT>
+__device__ inline uint32_t dma_offset(int it, int tid, int nkv) {
+  constexpr int GPR = D * (int)sizeof(T) / 16;
+  const int slot = it * NT + tid;
+  const int row = slot / GPR, pg = slot - row * GPR;
+  const int srow = min(row, nkv - 1);
+  return (uint32_t)((srow * GPR + (pg ^ swz(row))) * 16);
 }
 
 template <typename T, typename TO, int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(const T* __restrict__ Q,
-                                                           const T* __restrict__ K,
-                                                           const T* __restrict__ V,
-                                                           TO* __restrict__ O,
-                                                           const int32_t* __restrict__ row_ptr,
-                                                           const int32_t* __restrict__ col_idx,
-                                                           int H, int N, int Nb, int total_rows,
-                                                           float scale_log2, AttnArgs meta) {
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, TO* __restrict__ O,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int N, int Nb,
+    int total_rows, float scale_log2, AttnArgs meta) {
   constexpr int kWaves = BLK / 32;
   constexpr int NT = 64 * kWaves;
   constexpr int G = Elem<T>::kGran;
@@ -166,6 +184,9 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int kPv = BLK / 16;    // k-steps of O^T = V^T P^T
   constexpr int kOut = D / 32;     // 32-column output subtiles
   constexpr bool kBf16 = sizeof(T) == 2;
+  // The running max is only moved when a row's max grows by more than this (log2 units):
+  // weights are then at most 2^8, exact up to rounding, and the O / l rescale is skipped.
+  constexpr float kRescaleSlack = 8.0f;
   static_assert(NG % NT == 0, "tile must split evenly over the workgroup");
   static_assert(GPR >= 8, "swizzle needs at least 8 granules per row");
 
@@ -200,6 +221,21 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
       }
     }
     const T* vt = reinterpret_cast<const T*>(Vt);
+    const uint32_t k_lds = lds_addr(Kt) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
+    const uint32_t v_lds = lds_addr(Vt) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
+    // full-tile transfer offsets, shared by K and V (same layout)
+    uint32_t off[NLD];
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) off[it] = dma_offset<T, D, BLK, NT>(it, tid, BLK);
+    auto dma_block = [&](const T* src, uint32_t lds, int nkv) {
+      if (nkv == BLK) {
+        static_for<NLD>([&](auto it) { dma16<it.value * NT * 16>(src, off[it.value], lds); });
+      } else {
+        static_for<NLD>([&](auto it) {
+          dma16<it.value * NT * 16>(src, dma_offset<T, D, BLK, NT>(it.value, tid, nkv), lds);
+        });
+      }
+    };
     // Kept block indices of this row, 64 at a time, one per lane (read back with readlane).
     int cbase = e0;
     int cvec = e0 + lane < e1 ? col_idx[e0 + lane] : 0;
@@ -208,8 +244,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
     int c = __builtin_amdgcn_readlane(cvec, 0);
     {
       const int nkv = min(BLK, N - c * BLK);
-      dma_tile<T, D, BLK, NT>(Kt, K + head + (size_t)c * BLK * D, nkv, tid);
-      dma_tile<T, D, BLK, NT>(Vt, V + head + (size_t)c * BLK * D, nkv, tid);
+      dma_block(K + head + (size_t)c * BLK * D, k_lds, nkv);
+      dma_block(V + head + (size_t)c * BLK * D, v_lds, nkv);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
@@ -249,51 +285,60 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
       wg_barrier();   // every wave is done with K(e)
-      if (more) dma_tile<T, D, BLK, NT>(Kt, K + head + (size_t)cn * BLK * D, nkv_n, tid);
+      if (more) dma_block(K + head + (size_t)cn * BLK * D, k_lds, nkv_n);
 
-      // scale (log2 domain), mask keys past N, row max
-      float mx = -INFINITY;
+      // keys past N exist only in the last, partial key block
+      if (nkv < BLK) {
 #pragma unroll
-      for (int is = 0; is < kSub; ++is) {
+        for (int is = 0; is < kSub; ++is)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = 32 * is + 8 * (i >> 2) + 4 * hf + (i & 3);
-          float v = s[is][i] * scale_log2;
-          if (kk >= nkv) v = -INFINITY;
-          s[is][i] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int i = 0; i < 16; ++i)
+            if (32 * is + 8 * (i >> 2) + 4 * hf + (i & 3) >= nkv) s[is][i] = -INFINITY;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.f;
+      // row max of the raw scores (scale > 0 commutes with max), both lane halves
+      float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
+#pragma unroll
+      for (int is = 0; is < kSub; ++is)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mc[(i >> 1) & 3] = max3(mc[(i >> 1) & 3], s[is][i], s[is][i + 1]);
+      float mx = max3(mc[0], mc[1], max3(mc[2], mc[3], mc[3]));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+      }
+      const float m_tile = mx * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+        const float m_new = __builtin_fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
+      }
+      const float neg_m = -m_run;
       Frag<T> pf[kPv];
 #pragma unroll
       for (int u = 0; u < kPv; ++u) {
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = __builtin_amdgcn_exp2f(s[u >> 1][8 * (u & 1) + j] - m_new);
+        for (int j = 0; j < 8; ++j)
+          pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_m));
         if constexpr (kBf16) {
-          uint16_t b[8];
+          uint32_t wd[4];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            b[j] = f32_to_bf16_rne(pv[j]);
-            lsum += bf16_bits_to_f32(b[j]);
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2_t pk = {static_cast<__bf16>(pv[2 * j]), static_cast<__bf16>(pv[2 * j + 1])};
+            wd[j] = __builtin_bit_cast(uint32_t, pk);
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
           }
-          pf[u].v = make_uint4((uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16),
-                               (uint32_t)b[4] | ((uint32_t)b[5] << 16), (uint32_t)b[6] | ((uint32_t)b[7] << 16));
+          pf[u].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
         } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) lsum += pv[j];
+          for (int j = 0; j < 8; ++j) l_run += pv[j];
           pf[u].a = make_float4(pv[0], pv[1], pv[2], pv[3]);
           pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
         }
       }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
 
       // V(e) landed (K(e+1) may still be in flight)
       if (more) {
@@ -341,13 +386,17 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
       }
       wg_barrier();   // every wave is done with V(e)
-      if (more) dma_tile<T, D, BLK, NT>(Vt, V + head + (size_t)cn * BLK * D, nkv_n, tid);
+      if (more) dma_block(V + head + (size_t)cn * BLK * D, v_lds, nkv_n);
       c = cn;
     }
   }
 
   // epilogue: O = acc / l   (zero for empty rows and skipped heads)
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < N) {
     TO* orow = O + head + (size_t)qi * D;
