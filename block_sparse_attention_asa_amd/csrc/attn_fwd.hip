@@ -119,11 +119,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane L reads
-// 16 bytes at gbase + voff and they land at LDS byte address lds_base + 16 * L.  Written as
-// an asm block so that the compiler's wait insertion does not serialize it against
-// unrelated LDS reads; the instruction has no register results, and every reader of the
-// destination waits on vmcnt and a barrier first.  M0 carries the LDS base (one wait state
-// after writing it).
+// 16 bytes at gbase + voff and they land at LDS byte address lds_base + kLdsOff + 16 * L.
+// Written as an asm block so that the compiler's wait insertion does not serialize it
+// against unrelated LDS reads; the instruction has no register results, and every reader
+// of the destination waits on vmcnt and a barrier first.  The block may only touch M0 (the
+// LDS base; one wait state after writing it), which the compiler does not use in these
+// kernels: s_mov_b32 leaves SCC alone, unlike an s_add into M0 would.
 template <int kLdsOff>
 __device__ inline void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
   const uint64_t g = reinterpret_cast<uint64_t>(gbase);
@@ -131,12 +132,13 @@ __device__ inline void dma16(const void* gbase, uint32_t voff, uint32_t lds_base
   const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(g >> 32));
   const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)g);
   const uint64_t gu = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_base + (uint32_t)kLdsOff));
   asm volatile(
-      "s_add_u32 m0, %0, %3\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(gu), "i"(kLdsOff)
+      : "s"(m0v), "v"(voff), "s"(gu)
       : "memory");
 }
 
@@ -155,11 +157,11 @@ __device__ inline void static_for_impl(F&& f) {
 template <int N_, typename F>
 __device__ inline void static_for(F&& f) { static_for_impl<0, N_>(f); }
 
-// Per-thread byte offsets (within one key block) of the 16-byte granules this thread
-// transfers: instruction `it` of wave w fills LDS granule slots it*NT + 64*w + lane, which
-// hold logical granule (slot % GPR) ^ swz(row) of row slot / GPR.  Rows at or past nkv
-// re-read row nkv-1 (finite data that the softmax masks out).
-template <typename T, int D, int BLK, int NT>
+// Per-thread byte offsets (within one key step of KT rows) of the 16-byte granules this
+// thread transfers: instruction `it` of wave w fills LDS granule slots it*NT + 64*w + lane,
+// which hold logical granule (slot % GPR) ^ swz(row) of row slot / GPR.  Rows at or past
+// nkv re-read row nkv-1 (finite data that the softmax masks out).
+template <typename T, int D, int NT>
 __device__ inline uint32_t dma_offset(int it, int tid, int nkv) {
   constexpr int GPR = D * (int)sizeof(T) / 16;
   const int slot = it * NT + tid;
@@ -168,30 +170,36 @@ __device__ inline uint32_t dma_offset(int it, int tid, int nkv) {
   return (uint32_t)((srow * GPR + (pg ^ swz(row))) * 16);
 }
 
+// Each kept key block is consumed in steps of KT keys.  K and V of a step share one slot of
+// a two-slot LDS ring: while the workgroup computes on one slot, the next step's K and V
+// stream into the other, so a step needs a single barrier.
 template <typename T, typename TO, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, TO* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int N, int Nb,
     int total_rows, float scale_log2, AttnArgs meta) {
+  constexpr int KT = 64;           // keys per step
+  constexpr int kSteps = BLK / KT; // steps per key block
   constexpr int kWaves = BLK / 32;
   constexpr int NT = 64 * kWaves;
   constexpr int G = Elem<T>::kGran;
   constexpr int GPR = D * (int)sizeof(T) / 16;
-  constexpr int NG = BLK * GPR;
-  constexpr int NLD = NG / NT;     // DMA instructions per thread per tile
+  constexpr int NGS = KT * GPR;    // granules per step tile
+  constexpr int NLD = NGS / NT;    // DMA instructions per thread per step tile
   constexpr int kQk = D / 16;      // k-steps of S^T = K Q^T
-  constexpr int kSub = BLK / 32;   // 32-key subtiles per key block
-  constexpr int kPv = BLK / 16;    // k-steps of O^T = V^T P^T
+  constexpr int kSub = KT / 32;    // 32-key subtiles per step
+  constexpr int kPv = KT / 16;     // k-steps of O^T = V^T P^T
   constexpr int kOut = D / 32;     // 32-column output subtiles
   constexpr bool kBf16 = sizeof(T) == 2;
   // The running max is only moved when a row's max grows by more than this (log2 units):
   // weights are then at most 2^8, exact up to rounding, and the O / l rescale is skipped.
   constexpr float kRescaleSlack = 8.0f;
-  static_assert(NG % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(NGS % NT == 0, "tile must split evenly over the workgroup");
   static_assert(GPR >= 8, "swizzle needs at least 8 granules per row");
+  static_assert(BLK % KT == 0, "block must be a whole number of steps");
 
-  __shared__ uint4 Kt[NG];
-  __shared__ uint4 Vt[NG];
+  __shared__ uint4 Kt[2][NGS];
+  __shared__ uint4 Vt[2][NGS];
 
   const int row = xcd_row(blockIdx.x, total_rows);
   const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
@@ -220,52 +228,68 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
         qf[t] = Frag<T>{};
       }
     }
-    const T* vt = reinterpret_cast<const T*>(Vt);
-    const uint32_t k_lds = lds_addr(Kt) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
-    const uint32_t v_lds = lds_addr(Vt) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
-    // full-tile transfer offsets, shared by K and V (same layout)
+    const uint32_t wave_off = (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
+    const uint32_t k_lds[2] = {lds_addr(Kt[0]) + wave_off, lds_addr(Kt[1]) + wave_off};
+    const uint32_t v_lds[2] = {lds_addr(Vt[0]) + wave_off, lds_addr(Vt[1]) + wave_off};
+    // full-step transfer offsets, shared by K and V (same layout)
     uint32_t off[NLD];
 #pragma unroll
-    for (int it = 0; it < NLD; ++it) off[it] = dma_offset<T, D, BLK, NT>(it, tid, BLK);
-    auto dma_block = [&](const T* src, uint32_t lds, int nkv) {
-      if (nkv == BLK) {
-        static_for<NLD>([&](auto it) { dma16<it.value * NT * 16>(src, off[it.value], lds); });
+    for (int it = 0; it < NLD; ++it) off[it] = dma_offset<T, D, NT>(it, tid, KT);
+    auto dma_step = [&](const T* ksrc, const T* vsrc, int slot, int nv) {
+      if (nv == KT) {
+        static_for<NLD>([&](auto it) {
+          dma16<it.value * NT * 16>(ksrc, off[it.value], k_lds[slot]);
+          dma16<it.value * NT * 16>(vsrc, off[it.value], v_lds[slot]);
+        });
       } else {
         static_for<NLD>([&](auto it) {
-          dma16<it.value * NT * 16>(src, dma_offset<T, D, BLK, NT>(it.value, tid, nkv), lds);
+          const uint32_t o = dma_offset<T, D, NT>(it.value, tid, nv);
+          dma16<it.value * NT * 16>(ksrc, o, k_lds[slot]);
+          dma16<it.value * NT * 16>(vsrc, o, v_lds[slot]);
         });
       }
     };
     // Kept block indices of this row, 64 at a time, one per lane (read back with readlane).
     int cbase = e0;
     int cvec = e0 + lane < e1 ? col_idx[e0 + lane] : 0;
-    // prologue: K and V of the first kept block; then drain every outstanding load so the
-    // loop below starts with only its own transfers in flight
+    // current step: block e (index c, nkv valid keys), step hh within it
+    int e = e0, hh = 0;
     int c = __builtin_amdgcn_readlane(cvec, 0);
+    int nkv = min(BLK, N - c * BLK);
+    int slot = 0;
     {
-      const int nkv = min(BLK, N - c * BLK);
-      dma_block(K + head + (size_t)c * BLK * D, k_lds, nkv);
-      dma_block(V + head + (size_t)c * BLK * D, v_lds, nkv);
+      const size_t src = head + (size_t)c * BLK * D;
+      dma_step(K + src, V + src, 0, min(KT, nkv));
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-    for (int e = e0; e < e1; ++e) {
-      const int nkv = min(BLK, N - c * BLK);
-      const bool more = e + 1 < e1;
-      int cn = 0;
-      if (more) {
-        if (e + 1 - cbase == 64) {   // next batch of indices (rows longer than 64 blocks)
-          cbase += 64;
-          cvec = cbase + lane < e1 ? col_idx[cbase + lane] : 0;
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // rare: drains the tile transfers too
+    for (;;) {
+      // the step after this one (skips steps holding no valid key)
+      int e_n = e, hh_n = hh + 1, c_n = c, nkv_n = nkv;
+      if (hh_n >= kSteps || hh_n * KT >= nkv) {
+        e_n = e + 1;
+        hh_n = 0;
+        if (e_n < e1) {
+          if (e_n - cbase == 64) {   // next batch of indices (rows longer than 64 blocks)
+            cbase += 64;
+            cvec = cbase + lane < e1 ? col_idx[cbase + lane] : 0;
+          }
+          c_n = __builtin_amdgcn_readlane(cvec, e_n - cbase);
+          nkv_n = min(BLK, N - c_n * BLK);
         }
-        cn = __builtin_amdgcn_readlane(cvec, e + 1 - cbase);
       }
-      const int nkv_n = min(BLK, N - cn * BLK);
+      const bool more = e_n < e1;
+      const int nv = min(KT, nkv - hh * KT);   // valid keys in this step (>= 1)
 
-      // K(e) landed (V(e) may still be in flight)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD));
+      // this step's K and V landed everywhere; every wave is done with the other slot
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       wg_barrier();
+      if (more) {
+        const size_t src = head + ((size_t)c_n * BLK + hh_n * KT) * D;
+        dma_step(K + src, V + src, slot ^ 1, min(KT, nkv_n - hh_n * KT));
+      }
+      const uint4* kt = Kt[slot];
+      const T* vt = reinterpret_cast<const T*>(Vt[slot]);
+
       // S^T = K Q^T
       f32x16_t s[kSub];
 #pragma unroll
@@ -276,24 +300,21 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int t = 0; t < kQk; ++t) {
           Frag<T> a;
           if constexpr (kBf16) {
-            a.v = Kt[kr * GPR + ((2 * t + hf) ^ swz(kr))];
+            a.v = kt[kr * GPR + ((2 * t + hf) ^ swz(kr))];
           } else {
-            a.a = *reinterpret_cast<const float4*>(&Kt[kr * GPR + ((4 * t + 2 * hf) ^ swz(kr))]);
-            a.b = *reinterpret_cast<const float4*>(&Kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz(kr))]);
+            a.a = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf) ^ swz(kr))]);
+            a.b = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz(kr))]);
           }
           mma_k16(s[is], a, qf[t]);
         }
       }
-      wg_barrier();   // every wave is done with K(e)
-      if (more) dma_block(K + head + (size_t)cn * BLK * D, k_lds, nkv_n);
-
       // keys past N exist only in the last, partial key block
-      if (nkv < BLK) {
+      if (nv < KT) {
 #pragma unroll
         for (int is = 0; is < kSub; ++is)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (32 * is + 8 * (i >> 2) + 4 * hf + (i & 3) >= nkv) s[is][i] = -INFINITY;
+            if (32 * is + 8 * (i >> 2) + 4 * hf + (i & 3) >= nv) s[is][i] = -INFINITY;
       }
       // row max of the raw scores (scale > 0 commutes with max), both lane halves
       float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
@@ -339,14 +360,6 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
           pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
         }
       }
-
-      // V(e) landed (K(e+1) may still be in flight)
-      if (more) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLD));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      }
-      wg_barrier();
       // O^T += V^T P^T
 #pragma unroll
       for (int io = 0; io < kOut; ++io) {
@@ -385,9 +398,12 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
           mma_k16(acc[io], a, pf[u]);
         }
       }
-      wg_barrier();   // every wave is done with V(e)
-      if (more) dma_block(V + head + (size_t)cn * BLK * D, v_lds, nkv_n);
-      c = cn;
+      if (!more) break;
+      e = e_n;
+      hh = hh_n;
+      c = c_n;
+      nkv = nkv_n;
+      slot ^= 1;
     }
   }
 
