@@ -82,12 +82,19 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
 }
 __device__ inline float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// LDS tile layout (K and V alike): row-major [BLK keys][D], no padding, 16-byte granules
-// XOR-swizzled per row.  Physical granule = logical granule ^ swz(row).  swz maps 8
-// consecutive rows to 8 distinct values (conflict-free 16-byte K-fragment reads across 8
-// lanes) and any 4 consecutive rows starting at a multiple of 4 to {2m + b} (conflict-free
-// transpose reads of 2 adjacent granules x 4 rows).
-__device__ inline int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// LDS tile layout (K and V alike): row-major [keys][D], no padding, 16-byte granules
+// XOR-swizzled per row: physical granule = logical granule ^ swz(row).  gfx950 LDS serves
+// 256 bytes (64 banks) per cycle: 16 lanes of a 16-byte read or 32 lanes of an 8-byte read.
+// For rows of >= 16 granules, swz(r) = 4*(r%4) + (r/4)%4 is distinct over any 16
+// consecutive rows (conflict-free K-fragment reads: 16 lanes, 16 rows, one logical
+// granule) and, inside every aligned 4-row group, changes only bits 2-3 (conflict-free
+// transpose reads: 32 lanes covering 4 rows x 4 adjacent granules).  Rows of 8 granules
+// (bf16, d = 64) use a 3-bit variant.
+template <int GPR>
+__device__ inline int swz(int row) {
+  if constexpr (GPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return ((row & 3) << 1) | ((row >> 2) & 1);
+}
 
 // Workgroup id -> row, keeping consecutive rows (same head) on one XCD: dispatch assigns
 // workgroup ids round-robin over the 8 XCDs, so XCD x receives ids x, x+8, ...
@@ -167,7 +174,7 @@ __device__ inline uint32_t dma_offset(int it, int tid, int nkv) {
   const int slot = it * NT + tid;
   const int row = slot / GPR, pg = slot - row * GPR;
   const int srow = min(row, nkv - 1);
-  return (uint32_t)((srow * GPR + (pg ^ swz(row))) * 16);
+  return (uint32_t)((srow * GPR + (pg ^ swz<GPR>(row))) * 16);
 }
 
 // Each kept key block is consumed in steps of KT keys.  K and V of a step share one slot of
@@ -300,10 +307,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
         for (int t = 0; t < kQk; ++t) {
           Frag<T> a;
           if constexpr (kBf16) {
-            a.v = kt[kr * GPR + ((2 * t + hf) ^ swz(kr))];
+            a.v = kt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
           } else {
-            a.a = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf) ^ swz(kr))]);
-            a.b = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz(kr))]);
+            a.a = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf) ^ swz<GPR>(kr))]);
+            a.b = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz<GPR>(kr))]);
           }
           mma_k16(s[is], a, qf[t]);
         }
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
               const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
-              const int gran = (dcol >> 3) ^ swz(kr);
+              const int gran = (dcol >> 3) ^ swz<GPR>(kr);
               const uint16_t* p = vt + kr * D + gran * 8 + (dcol & 7);
               part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                   (__attribute__((address_space(3))) short4_t*)(p));
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
               const int kr = 16 * u + 8 * (jj >> 2) + 4 * hf + (jj & 3);
-              av[jj] = vt[(kr * GPR + ((d / G) ^ swz(kr))) * G + (d % G)];
+              av[jj] = vt[(kr * GPR + ((d / G) ^ swz<GPR>(kr))) * G + (d % G)];
             }
             a.a = make_float4(av[0], av[1], av[2], av[3]);
             a.b = make_float4(av[4], av[5], av[6], av[7]);
