@@ -12,8 +12,7 @@
 //
 // Pipeline (all on the caller's stream):
 //   pool_kernel      Q, K -> Qp [B,H,Nb,d], KpT [B,H,d,Nb] (float64 means); HBM-bound.
-//   score_kernel     S = Qp KpT / sqrt(d), 16 query blocks per workgroup so each
-//                    pooled-key panel is read once per 16 rows.
+//   score_kernel     S = Qp KpT / sqrt(d), 64 x 64 tiles through LDS, 4 x 4 per thread.
 //   select_kernel    one workgroup per row: softmax, bitonic sort of (P, c) in LDS,
 //                    prefix selection, union with forced / static blocks -> bitmask.
 //   static_kernel    one wavefront per row: static pattern bitmask only.
@@ -27,7 +26,6 @@ namespace asa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kScoreRows = 16;   // query blocks per score workgroup
 
 __device__ inline double bf16_to_f64(uint16_t x) {
   return (double)__uint_as_float(((uint32_t)x) << 16);
@@ -129,59 +127,84 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 }
 
 // ------------------------------------------------------------------ block scores
-// grid = B*H*ceil(Nb/16); each workgroup scores 16 query blocks against all key blocks.
+// One workgroup computes a 64 x 64 tile of S for one head: query blocks r0.., key blocks
+// c0...  The pooled rows are staged through LDS in 32-wide slices of d; each thread owns a
+// 4 x 4 sub-tile (rows tr + 16i, columns tc + 16j) and accumulates in float64 in a fixed
+// order over d.  grid = B*H * ceil(Nb/64)^2.
+constexpr int kST = 64;   // score tile edge
+constexpr int kSD = 32;   // d slice
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qp,
                                                          const double* __restrict__ kpt,
                                                          double* __restrict__ score, int Nb) {
-  __shared__ double qs[kScoreRows][D];
-  const int groups = (Nb + kScoreRows - 1) / kScoreRows;
-  const int bh = blockIdx.x / groups;
-  const int r0 = (blockIdx.x - bh * groups) * kScoreRows;
-  const int nr = min(kScoreRows, Nb - r0);
-  for (int i = threadIdx.x; i < kScoreRows * D; i += kThreads) {
-    const int rr = i / D, j = i - rr * D;
-    qs[rr][j] = rr < nr ? qp[((size_t)bh * Nb + r0 + rr) * D + j] : 0.0;
-  }
-  __syncthreads();
+  __shared__ double qs[kST][kSD + 1];
+  __shared__ double ks[kSD][kST + 1];
+  const int tiles = (Nb + kST - 1) / kST;
+  int id = blockIdx.x;
+  const int tcol = id % tiles;
+  id /= tiles;
+  const int trow = id % tiles, bh = id / tiles;
+  const int r0 = trow * kST, c0 = tcol * kST;
+  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const double* q = qp + (size_t)bh * Nb * D;
   const double* kt = kpt + (size_t)bh * D * Nb;
-  const double sqrt_d = sqrt((double)D);
-  for (int c = threadIdx.x; c < Nb; c += kThreads) {
-    double acc[kScoreRows];
+  double acc[4][4];
 #pragma unroll
-    for (int rr = 0; rr < kScoreRows; ++rr) acc[rr] = 0.0;
-    for (int j = 0; j < D; ++j) {
-      const double kv = kt[(size_t)j * Nb + c];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int rr = 0; rr < kScoreRows; ++rr) acc[rr] = fma(qs[rr][j], kv, acc[rr]);
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int d0 = 0; d0 < D; d0 += kSD) {
+    for (int e = tid; e < kST * kSD; e += kThreads) {
+      const int rr = e / kSD, dd = e - rr * kSD;            // q: row-major, d fastest
+      qs[rr][dd] = r0 + rr < Nb ? q[(size_t)(r0 + rr) * D + d0 + dd] : 0.0;
+      const int d2 = e / kST, cc = e - d2 * kST;            // k: transposed, block fastest
+      ks[d2][cc] = c0 + cc < Nb ? kt[(size_t)(d0 + d2) * Nb + c0 + cc] : 0.0;
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int dd = 0; dd < kSD; ++dd) {
+      double qv[4], kv[4];
 #pragma unroll
-    for (int rr = 0; rr < kScoreRows; ++rr)
-      if (rr < nr) score[((size_t)bh * Nb + r0 + rr) * Nb + c] = acc[rr] / sqrt_d;
+      for (int i = 0; i < 4; ++i) qv[i] = qs[tr + 16 * i][dd];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kv[j] = ks[dd][tc + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(qv[i], kv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const double sqrt_d = sqrt((double)D);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + tr + 16 * i;
+    if (r >= Nb) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + tc + 16 * j;
+      if (c < Nb) score[((size_t)bh * Nb + r) * Nb + c] = acc[i][j] / sqrt_d;
+    }
   }
 }
 
 // ------------------------------------------------------------------ block reductions
+// Workgroup reductions: butterfly within each wavefront, then the 4 wave results in a fixed
+// order (deterministic).  scratch holds at least 4 doubles.
 __device__ inline double block_reduce_max(double v, double* scratch) {
-  scratch[threadIdx.x] = v;
+  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) scratch[threadIdx.x] = fmax(scratch[threadIdx.x], scratch[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const double r = scratch[0];
+  const double r = fmax(fmax(scratch[0], scratch[1]), fmax(scratch[2], scratch[3]));
   __syncthreads();
   return r;
 }
 
 __device__ inline double block_reduce_sum(double v, double* scratch) {
-  scratch[threadIdx.x] = v;
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) scratch[threadIdx.x] += scratch[threadIdx.x + s];
-    __syncthreads();
-  }
-  const double r = scratch[0];
+  const double r = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
   __syncthreads();
   return r;
 }
@@ -327,29 +350,42 @@ __global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__
 // ------------------------------------------------------------------ CSR
 constexpr int kScanThreads = 1024;
 
-// Single workgroup: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].
+// Single workgroup: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].  Each thread owns a
+// run of consecutive rows; one wave-level scan of the per-thread totals.
 __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* __restrict__ count,
                                                                 int32_t* __restrict__ row_ptr,
                                                                 int rows) {
-  __shared__ int buf[kScanThreads];
-  __shared__ int carry;
-  if (threadIdx.x == 0) { carry = 0; row_ptr[0] = 0; }
+  __shared__ int wsum[kScanThreads / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (rows + kScanThreads - 1) / kScanThreads;
+  const int t0 = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (t0 + i < rows) local += count[t0 + i];
+  int incl = local;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  for (int base = 0; base < rows; base += kScanThreads) {
-    const int i = base + threadIdx.x;
-    int v = i < rows ? count[i] : 0;
-    buf[threadIdx.x] = v;
-    __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele scan
-      const int add = threadIdx.x >= off ? buf[threadIdx.x - off] : 0;
-      __syncthreads();
-      buf[threadIdx.x] += add;
-      __syncthreads();
+  if (wv == 0) {
+    const int v0 = lane < kScanThreads / 64 ? wsum[lane] : 0;
+    int x = v0;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(x, off, 64);
+      if (lane >= off) x += v;
     }
-    if (i < rows) row_ptr[i + 1] = carry + buf[threadIdx.x];
-    __syncthreads();
-    if (threadIdx.x == kScanThreads - 1) carry += buf[threadIdx.x];
-    __syncthreads();
+    if (lane < kScanThreads / 64) wsum[lane] = x - v0;   // exclusive
+  }
+  __syncthreads();
+  int run = wsum[wv] + incl - local;
+  if (threadIdx.x == 0) row_ptr[0] = 0;
+  for (int i = 0; i < per; ++i) {
+    if (t0 + i < rows) {
+      run += count[t0 + i];
+      row_ptr[t0 + i + 1] = run;
+    }
   }
 }
 
@@ -420,8 +456,8 @@ hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& 
 }
 
 hipError_t launch_scores(const MaskGeom& g, const MaskWorkspace& ws, hipStream_t s) {
-  const int groups = (g.Nb + kScoreRows - 1) / kScoreRows;
-  const dim3 grid((unsigned)(g.B * g.H * groups));
+  const int tiles = (g.Nb + kST - 1) / kST;
+  const dim3 grid((unsigned)(g.B * g.H * tiles * tiles));
   if (g.d == 128)
     hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kThreads), 0, s, ws.qp, ws.kpt, ws.score, g.Nb);
   else
