@@ -70,16 +70,19 @@ def cpu_baseline(cfg, x, budget_s):
     M = O.build_mask(q64, k64, cfg.blk, mode=cfg.mode, k=cfg.k, keep_diag=cfg.keep_diag)
     t_mask = time.perf_counter() - t0
     total_flops = O.kept_tile_flops(M, cfg.N, cfg.blk, cfg.d)
-    # attention on whole query blocks of head 0 until the time budget is spent
+    # attention on whole query blocks, drawn at random over all heads, until the time
+    # budget is spent
     t_att, flops_done, blocks = 0.0, 0.0, 0
     rng = np.random.default_rng(0)
-    order = rng.permutation(cfg.Nb)
-    for r in order:
+    order = rng.permutation(cfg.B * cfg.H * cfg.Nb)
+    for idx in order:
+        b, rem = divmod(int(idx), cfg.H * cfg.Nb)
+        h, r = divmod(rem, cfg.Nb)
         t0 = time.perf_counter()
-        O.attention_block(q64, k64, v64, M, cfg.blk, 0, 0, int(r))
+        O.attention_block(q64, k64, v64, M, cfg.blk, b, h, r)
         t_att += time.perf_counter() - t0
-        lo, hi = O.block_range(int(r), cfg.N, cfg.blk)
-        flops_done += 4.0 * (hi - lo) * O.kept_tokens(M[0, 0, r], cfg.N, cfg.blk).size * cfg.d
+        lo, hi = O.block_range(r, cfg.N, cfg.blk)
+        flops_done += 4.0 * (hi - lo) * O.kept_tokens(M[b, h, r], cfg.N, cfg.blk).size * cfg.d
         blocks += 1
         if t_att + t_mask > budget_s:
             break
@@ -88,7 +91,7 @@ def cpu_baseline(cfg, x, budget_s):
         "value": total_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
         "sample": (f"float64 oracle: full adaptive mask build for all {cfg.H} heads ({t_mask:.2f} s) + "
-                   f"attention on {blocks} of {cfg.H * cfg.Nb} query blocks ({t_att:.2f} s), "
+                   f"attention on {blocks} of {cfg.B * cfg.H * cfg.Nb} query blocks drawn over all heads ({t_att:.2f} s), "
                    f"extrapolated by kept-tile flops to one step ({t_step:.1f} s)"),
         "step_seconds_extrapolated": t_step,
     }

@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/asa.h"
+#include "asa.h"
 #include "asa_internal.h"
 
 namespace {
