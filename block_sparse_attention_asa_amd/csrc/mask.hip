@@ -12,9 +12,10 @@
 //
 // Pipeline (all on the caller's stream):
 //   pool_kernel      Q, K -> Qp [B,H,Nb,d], KpT [B,H,d,Nb] (float64 means); HBM-bound.
-//   score_kernel     S = Qp KpT / sqrt(d), 64 x 64 tiles through LDS, 4 x 4 per thread.
-//   select_kernel    one workgroup per row: softmax, bitonic sort of (P, c) in LDS,
-//                    prefix selection, union with forced / static blocks -> bitmask.
+//   score_kernel     S = Qp KpT / sqrt(d), 32 x 32 tiles through LDS, 2 x 2 per thread.
+//   select_kernel    one workgroup per row: softmax, bitonic sort of (P, c) held in
+//                    registers (cross-lane, LDS or in-register exchanges), prefix
+//                    selection, union with forced / static blocks -> bitmask.
 //   static_kernel    one wavefront per row: static pattern bitmask only.
 //   csr_scan_kernel  exclusive scan of per-row counts -> row_ptr.
 //   csr_fill_kernel  one wavefront per row: bitmask -> ascending col_idx.
@@ -86,15 +87,26 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 
   if (BF16) {
     const uint16_t* x = static_cast<const uint16_t*>(blockIdx.y == 0 ? q : k) + head_off;
-    for (int i = sub; i < n; i += RPP) {
-      const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)(lo + i) * D + col);
+    auto add_row = [&](const uint4& v) {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[2 * j] += bf16_to_f64((uint16_t)(w[j] & 0xffffu));
         acc[2 * j + 1] += bf16_to_f64((uint16_t)(w[j] >> 16));
       }
+    };
+    // rows in the same order as one at a time, but a batch of loads in flight at once
+    constexpr int kBatch = 4;
+    int i = sub;
+    for (; i + (kBatch - 1) * RPP < n; i += kBatch * RPP) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        v[b] = *reinterpret_cast<const uint4*>(x + (size_t)(lo + i + b * RPP) * D + col);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) add_row(v[b]);
     }
+    for (; i < n; i += RPP) add_row(*reinterpret_cast<const uint4*>(x + (size_t)(lo + i) * D + col));
   } else {
     const float* x = static_cast<const float*>(blockIdx.y == 0 ? q : k) + head_off;
     for (int i = sub; i < n; i += RPP) {
@@ -127,12 +139,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 }
 
 // ------------------------------------------------------------------ block scores
-// One workgroup computes a 64 x 64 tile of S for one head: query blocks r0.., key blocks
+// One workgroup computes a 32 x 32 tile of S for one head: query blocks r0.., key blocks
 // c0...  The pooled rows are staged through LDS in 32-wide slices of d; each thread owns a
-// 4 x 4 sub-tile (rows tr + 16i, columns tc + 16j) and accumulates in float64 in a fixed
-// order over d.  grid = B*H * ceil(Nb/64)^2.
-constexpr int kST = 64;   // score tile edge
-constexpr int kSD = 32;   // d slice
+// 2 x 2 sub-tile (rows tr + 16i, columns tc + 16j) and accumulates in float64 in a fixed
+// order over d.  grid = B*H * ceil(Nb/32)^2, enough workgroups to fill the GPU even for a
+// few heads.
+constexpr int kST = 32;          // score tile edge
+constexpr int kSD = 32;          // d slice
+constexpr int kSP = kST / 16;    // outputs per thread along each tile edge
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qp,
                                                          const double* __restrict__ kpt,
@@ -148,12 +162,13 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restric
   const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
   const double* q = qp + (size_t)bh * Nb * D;
   const double* kt = kpt + (size_t)bh * D * Nb;
-  double acc[4][4];
+  double acc[kSP][kSP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kSP; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < kSP; ++j) acc[i][j] = 0.0;
   for (int d0 = 0; d0 < D; d0 += kSD) {
+#pragma unroll
     for (int e = tid; e < kST * kSD; e += kThreads) {
       const int rr = e / kSD, dd = e - rr * kSD;            // q: row-major, d fastest
       qs[rr][dd] = r0 + rr < Nb ? q[(size_t)(r0 + rr) * D + d0 + dd] : 0.0;
@@ -161,31 +176,36 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restric
       ks[d2][cc] = c0 + cc < Nb ? kt[(size_t)(d0 + d2) * Nb + c0 + cc] : 0.0;
     }
     __syncthreads();
-#pragma unroll 4
+#pragma unroll 8
     for (int dd = 0; dd < kSD; ++dd) {
-      double qv[4], kv[4];
+      double qv[kSP], kv[kSP];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qv[i] = qs[tr + 16 * i][dd];
+      for (int i = 0; i < kSP; ++i) qv[i] = qs[tr + 16 * i][dd];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kv[j] = ks[dd][tc + 16 * j];
+      for (int j = 0; j < kSP; ++j) kv[j] = ks[dd][tc + 16 * j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kSP; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(qv[i], kv[j], acc[i][j]);
+        for (int j = 0; j < kSP; ++j) acc[i][j] = fma(qv[i], kv[j], acc[i][j]);
     }
     __syncthreads();
   }
   const double sqrt_d = sqrt((double)D);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kSP; ++i) {
     const int r = r0 + tr + 16 * i;
     if (r >= Nb) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSP; ++j) {
       const int c = c0 + tc + 16 * j;
       if (c < Nb) score[((size_t)bh * Nb + r) * Nb + c] = acc[i][j] / sqrt_d;
     }
   }
+}
+
+// (p, c) comes before (q, e) in rank order: larger probability first, then smaller block.
+__device__ inline bool ranks_before(double p, int c, double q, int e) {
+  return p > q || (p == q && c < e);
 }
 
 // ------------------------------------------------------------------ block reductions
@@ -207,11 +227,6 @@ __device__ inline double block_reduce_sum(double v, double* scratch) {
   const double r = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
   __syncthreads();
   return r;
-}
-
-// (p, c) comes before (q, e) in rank order: larger probability first, then smaller block.
-__device__ inline bool ranks_before(double p, int c, double q, int e) {
-  return p > q || (p == q && c < e);
 }
 
 // ------------------------------------------------------------------ selection
@@ -256,58 +271,97 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       part += e;
     }
     const double z = block_reduce_sum(part, scratch);   // also a barrier for key[]
+    // Bitonic sort of (P, c) into rank order over np2 = 2^ceil(log2 Nb) slots.  Slot
+    // i = e*kThreads + tid lives in register e of thread tid.  A compare-exchange at
+    // distance j runs across lanes of one wavefront (j < 64, no barrier), through LDS
+    // (64 <= j < kThreads), or between a thread's own registers (j >= kThreads).
     int np2 = 1;
     while (np2 < Nb) np2 <<= 1;
-    for (int c = tid; c < np2; c += kThreads) {
-      if (c < Nb) {
-        key[c] = key[c] / z;
-        idx[c] = c;
-      } else {
-        key[c] = -1.0;           // padding ranks after every real block
-        idx[c] = 0x7fffffff;
-      }
+    constexpr int kPer = kMaxMaskBlocks / kThreads;
+    double kv[kPer];
+    int ki[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = e * kThreads + tid;
+      kv[e] = i < Nb ? key[i] / z : -1.0;   // padding ranks after every real block
+      ki[e] = i < Nb ? i : 0x7fffffff;
     }
-    __syncthreads();
-    // bitonic sort into rank order
+    // keep the first-ranked of (a, b) when `first`, else the other one
+    auto pick = [](double& a, int& ia, double b, int ib, bool first) {
+      const bool a_first = ranks_before(a, ia, b, ib);
+      if (a_first != first) { a = b; ia = ib; }
+    };
     for (int kk = 2; kk <= np2; kk <<= 1) {
       for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < np2; i += kThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const double a = key[i], b = key[ixj];
-            const int ia = idx[i], ib = idx[ixj];
-            const bool a_first = ranks_before(a, ia, b, ib);
-            const bool want_a_first = (i & kk) == 0;
-            if (a_first != want_a_first) {
-              key[i] = b; key[ixj] = a;
-              idx[i] = ib; idx[ixj] = ia;
+        if (j >= kThreads) {
+          const int je = j / kThreads;
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            const int e2 = e ^ je;
+            if (e2 > e && e2 < kPer) {
+              const int i = e * kThreads + tid;
+              const bool up = (i & kk) == 0;
+              double a = kv[e], b = kv[e2];
+              int ia = ki[e], ib = ki[e2];
+              if (ranks_before(a, ia, b, ib) != up) {
+                kv[e] = b; ki[e] = ib; kv[e2] = a; ki[e2] = ia;
+              }
+            }
+          }
+        } else if (j >= 64) {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            if (e * kThreads < np2) { key[e * kThreads + tid] = kv[e]; idx[e * kThreads + tid] = ki[e]; }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            const int i = e * kThreads + tid;
+            if (e * kThreads < np2) {
+              const int pi = i ^ j;
+              pick(kv[e], ki[e], key[pi], idx[pi], ((i & kk) == 0) == ((i & j) == 0));
+            }
+          }
+          __syncthreads();
+        } else {
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) {
+            if (e * kThreads < np2) {   // workgroup-uniform
+              const int i = e * kThreads + tid;
+              const double b = __shfl_xor(kv[e], j, 64);
+              const int ib = __shfl_xor(ki[e], j, 64);
+              pick(kv[e], ki[e], b, ib, ((i & kk) == 0) == ((i & j) == 0));
             }
           }
         }
-        __syncthreads();
       }
     }
     // length of the adaptive prefix
-    if (tid == 0) {
-      int m;
-      if (p.mode == 0) {
-        m = min(max(p.k, 0), Nb);
-      } else {
-        m = Nb;
+    if (p.mode == 0) {
+      if (tid == 0) kept_prefix = min(max(p.k, 0), Nb);
+    } else {
+      // running mass summed sequentially in rank order (the order fixes the float64 bits)
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (e * kThreads < np2) key[e * kThreads + tid] = kv[e];
+      __syncthreads();
+      if (tid == 0) {
+        int m = Nb;
         double mass = 0.0;
-        for (int t = 0; t < Nb; ++t) {   // sequential running sum in rank order
+        for (int t = 0; t < Nb; ++t) {
           mass += key[t];
           if (mass >= p.tau) { m = t + 1; break; }
         }
         if (p.k_cap > 0) m = min(m, p.k_cap);
+        kept_prefix = m;
       }
-      kept_prefix = m;
     }
     __syncthreads();
     const int m = kept_prefix;
-    for (int t = tid; t < m; t += kThreads) {
-      const int c = idx[t];
-      atomicOr(&word[c >> 5], 1u << (c & 31));
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = e * kThreads + tid;
+      if (i < m) atomicOr(&word[ki[e] >> 5], 1u << (ki[e] & 31));
     }
     for (int c = tid; c < Nb; c += kThreads) {
       const bool forced = (p.keep_diag && c == r) || (c < p.n_text_blocks) ||
