@@ -128,6 +128,7 @@ def main():
     rows = B * H * Nb
     row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(asa.asa_csr_capacity(B, H, N, blk), dtype=torch.int32, device=dev)
+    order = torch.empty(rows, dtype=torch.int32, device=dev)   # attention schedule
     shp = asa.asa_shape(B, H, N, d, blk, asa.ASA_BF16)
     import ctypes
     ws = torch.empty(int(asa.lib.asa_build_mask_workspace_size(ctypes.byref(shp))), dtype=torch.uint8,
@@ -136,15 +137,15 @@ def main():
 
     def build_mask():
         asa.asa_build_mask(xd["q"], xd["k"], blk, asa.TOPK, k_top=cfg.k, keep_diag=1,
-                           out=(row_ptr, col_idx), workspace=ws)
+                           out=(row_ptr, col_idx, order), workspace=ws)
 
-    def attend(rp, ci, o):
-        asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp, ci, blk, out=o)
+    def attend(rp, ci, o, od=None):
+        asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp, ci, blk, order=od, out=o)
 
     log("bench: warmup")
     for _ in range(args.warmup):
         build_mask()
-        attend(row_ptr, col_idx, out)
+        attend(row_ptr, col_idx, out, order)
     torch.cuda.synchronize()
     rp_h = row_ptr.cpu().numpy()
     ci_h = col_idx[: int(rp_h[-1])].cpu().numpy()
@@ -161,7 +162,7 @@ def main():
         ev[i][0].record(stream)
         build_mask()
         ev[i][1].record(stream)
-        attend(row_ptr, col_idx, out)
+        attend(row_ptr, col_idx, out, order)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

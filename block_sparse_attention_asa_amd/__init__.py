@@ -38,7 +38,8 @@ class asa_head_pattern(ctypes.Structure):
 
 
 class asa_csr(ctypes.Structure):
-    _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("capacity", ctypes.c_int64)]
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p), ("capacity", ctypes.c_int64),
+                ("order", ctypes.c_void_p)]
 
 
 EXPORTS = {
@@ -148,22 +149,48 @@ def _alloc_csr(B, H, N, blk, device):
     return row_ptr, col_idx
 
 
+def _csr_buffers(out, with_order, B, H, N, blk, device):
+    """(row_ptr, col_idx, order or None): the caller's buffers or fresh ones."""
+    if out is not None:
+        if len(out) not in (2, 3):
+            raise ValueError("out must be (row_ptr, col_idx) or (row_ptr, col_idx, order)")
+        row_ptr, col_idx = out[0], out[1]
+        order = out[2] if len(out) == 3 else None
+    else:
+        row_ptr, col_idx = _alloc_csr(B, H, N, blk, device)
+        order = None
+    if order is None and with_order:
+        order = torch.empty(row_ptr.numel() - 1, dtype=torch.int32, device=row_ptr.device)
+    if order is not None:
+        _require_device(order)
+        if order.dtype != torch.int32 or order.numel() != row_ptr.numel() - 1:
+            raise ValueError("order must be int32 with one entry per CSR row")
+    return row_ptr, col_idx, order
+
+
+def _csr_struct(row_ptr, col_idx, order):
+    return asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel(),
+                   order.data_ptr() if order is not None else None)
+
+
 def asa_build_mask(q: torch.Tensor, k: torch.Tensor, blk: int, mode: int, *, k_top: int = 0,
                    tau: float = 0.0, k_cap: int = 0, n_text: int = 0, keep_diag: int = 1,
                    patterns: Optional[Sequence[Tuple[int, int]]] = None,
-                   out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                   out: Optional[Tuple[torch.Tensor, ...]] = None, with_order: bool = False,
                    workspace: Optional[torch.Tensor] = None, stream=None):
     """Adaptive block mask (plus forced / static blocks) as CSR (row_ptr, col_idx).
 
-    col_idx is sized for the worst case; its first row_ptr[-1] entries are valid.
+    col_idx is sized for the worst case; its first row_ptr[-1] entries are valid.  With
+    with_order (or a 3-tuple `out`), also returns the attention schedule `order` (rows
+    longest first inside each XCD range; see asa.h).
     """
     _require_device(q, k)
     if q.shape != k.shape or q.dtype != k.dtype:
         raise ValueError("q and k must have the same shape and dtype")
     shp = _shape_of(q, blk)
     B, H, N, _ = q.shape
-    row_ptr, col_idx = out if out is not None else _alloc_csr(B, H, N, blk, q.device)
-    csr = asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+    row_ptr, col_idx, order = _csr_buffers(out, with_order, B, H, N, blk, q.device)
+    csr = _csr_struct(row_ptr, col_idx, order)
     ad = asa_adaptive(mode, k_top, tau, k_cap, n_text, keep_diag)
     need = int(lib.asa_build_mask_workspace_size(ctypes.byref(shp)))
     if workspace is None:
@@ -172,16 +199,17 @@ def asa_build_mask(q: torch.Tensor, k: torch.Tensor, blk: int, mode: int, *, k_t
     _check(lib.asa_build_mask(q.data_ptr(), k.data_ptr(), ctypes.byref(shp), ctypes.byref(ad),
                               pats, ctypes.byref(csr), workspace.data_ptr(), workspace.numel(),
                               _stream(q.device, stream)), "asa_build_mask")
-    return row_ptr, col_idx
+    return (row_ptr, col_idx) if order is None else (row_ptr, col_idx, order)
 
 
 def asa_static_mask(B: int, H: int, N: int, blk: int, patterns: Sequence[Tuple[int, int]],
-                    device, *, out=None, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Static-pattern block mask as CSR (row_ptr, col_idx)."""
+                    device, *, out=None, with_order: bool = False,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    """Static-pattern block mask as CSR (row_ptr, col_idx[, order])."""
     device = torch.device(device)
     shp = asa_shape(B, H, N, 64, blk, ASA_BF16)
-    row_ptr, col_idx = out if out is not None else _alloc_csr(B, H, N, blk, device)
-    csr = asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+    row_ptr, col_idx, order = _csr_buffers(out, with_order, B, H, N, blk, device)
+    csr = _csr_struct(row_ptr, col_idx, order)
     need = int(lib.asa_static_mask_workspace_size(ctypes.byref(shp)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
@@ -190,15 +218,20 @@ def asa_static_mask(B: int, H: int, N: int, blk: int, patterns: Sequence[Tuple[i
         raise ValueError("patterns are required")
     _check(lib.asa_static_mask(ctypes.byref(shp), pats, ctypes.byref(csr), workspace.data_ptr(),
                                workspace.numel(), _stream(device, stream)), "asa_static_mask")
-    return row_ptr, col_idx
+    return (row_ptr, col_idx) if order is None else (row_ptr, col_idx, order)
 
 
 def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
                       col_idx: torch.Tensor, blk: int, *,
                       patterns: Optional[Sequence[Tuple[int, int]]] = None,
                       out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
+                      order: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Block-sparse attention over the kept tiles of the CSR mask; returns O [B,H,N,d]."""
+    """Block-sparse attention over the kept tiles of the CSR mask; returns O [B,H,N,d].
+
+    `order`, from a mask builder's with_order, sets the processing order of the rows; the
+    result does not depend on it.
+    """
     _require_device(q, k, v, row_ptr, col_idx)
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share shape and dtype")
@@ -212,7 +245,11 @@ def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     _require_device(out)
     o_code = _dtype_code(out)
-    csr = asa_csr(row_ptr.data_ptr(), col_idx.data_ptr(), col_idx.numel())
+    if order is not None:
+        _require_device(order)
+        if order.dtype != torch.int32 or order.numel() != row_ptr.numel() - 1:
+            raise ValueError("order must be int32 with one entry per CSR row")
+    csr = _csr_struct(row_ptr, col_idx, order)
     pats = _patterns(patterns, H)
     _check(lib.asa_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), o_code,
                                  ctypes.byref(shp), ctypes.byref(csr), pats, float(scale),

@@ -114,7 +114,7 @@ asa_status check_workspace(void* ws, size_t have, size_t need) {
 
 extern "C" {
 
-int32_t asa_version(void) { return 10000; }
+int32_t asa_version(void) { return 10100; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {
@@ -189,7 +189,7 @@ asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
   if ((e = asa::launch_pool(Q, K, shape->in_dtype == ASA_BF16, g, ws, s)) != hipSuccess) return hip_fail(e, "pool");
   if ((e = asa::launch_scores(g, ws, s)) != hipSuccess) return hip_fail(e, "scores");
   if ((e = asa::launch_select(g, p, heads, ws, s)) != hipSuccess) return hip_fail(e, "select");
-  if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, s)) != hipSuccess) return hip_fail(e, "csr");
+  if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, out->order, s)) != hipSuccess) return hip_fail(e, "csr");
   return ASA_OK;
 }
 
@@ -211,7 +211,7 @@ asa_status asa_static_mask(const asa_shape* shape, const asa_head_pattern* patte
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if ((e = asa::launch_static_rows(g, heads, ws, s)) != hipSuccess) return hip_fail(e, "static rows");
-  if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, s)) != hipSuccess) return hip_fail(e, "csr");
+  if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, out->order, s)) != hipSuccess) return hip_fail(e, "csr");
   return ASA_OK;
 }
 
@@ -234,6 +234,7 @@ asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* 
   a.q = Q; a.k = K; a.v = V; a.o = O;
   a.row_ptr = csr->row_ptr;
   a.col_idx = csr->col_idx;
+  a.order = csr->order;
   a.B = shape->B; a.H = shape->H; a.N = shape->N; a.d = shape->d; a.blk = shape->blk;
   a.Nb = (int)num_blocks(shape);
   a.in_bf16 = shape->in_dtype == ASA_BF16;

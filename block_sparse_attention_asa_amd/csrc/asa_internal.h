@@ -10,6 +10,16 @@ namespace asa {
 
 constexpr int kMaxHeads = 256;       // per-head pattern table travels as a kernel argument
 constexpr int kMaxMaskBlocks = 1024; // row bitmask (32 words) and LDS sort width
+constexpr int kXcds = 8;             // accelerator complex dies sharing one dispatcher
+
+// Rows [lo, hi) of the `total` CSR rows form the contiguous range processed on XCD x.
+// Dispatch hands workgroup ids to the XCDs round-robin; the attention kernel maps the ids
+// an XCD receives onto its range, and the mask builders order rows inside each range.
+__host__ __device__ inline void xcd_range(int x, int total, int& lo, int& hi) {
+  const int per = total / kXcds, rem = total % kXcds;
+  lo = x * per + (x < rem ? x : rem);
+  hi = lo + per + (x < rem ? 1 : 0);
+}
 
 // Per-head pattern table passed by value (2 KiB of kernel arguments).
 struct HeadTable {
@@ -46,7 +56,7 @@ hipError_t launch_select(const MaskGeom& g, const AdaptiveParams& p, const HeadT
 hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const MaskWorkspace& ws,
                               hipStream_t s);
 hipError_t launch_csr(const MaskGeom& g, const MaskWorkspace& ws, int32_t* row_ptr,
-                      int32_t* col_idx, hipStream_t s);
+                      int32_t* col_idx, int32_t* order, hipStream_t s);
 
 // Attention forward.
 struct AttnArgs {
@@ -56,6 +66,7 @@ struct AttnArgs {
   void* o;
   const int32_t* row_ptr;
   const int32_t* col_idx;
+  const int32_t* order;  // processing order of the rows, or NULL for row order
   int32_t B, H, N, d, blk, Nb;
   bool in_bf16, out_bf16;
   float scale_log2;      // softmax scale times log2(e)

@@ -99,10 +99,9 @@ __device__ inline int swz(int row) {
 // Workgroup id -> row, keeping consecutive rows (same head) on one XCD: dispatch assigns
 // workgroup ids round-robin over the 8 XCDs, so XCD x receives ids x, x+8, ...
 __device__ inline int xcd_row(int wg, int total) {
-  constexpr int kXcd = 8;
-  const int per = total / kXcd, rem = total % kXcd;
-  const int x = wg % kXcd, local = wg / kXcd;
-  return x * per + min(x, rem) + local;
+  int lo, hi;
+  xcd_range(wg % kXcds, total, lo, hi);
+  return lo + wg / kXcds;
 }
 
 template <typename T> struct Elem;
@@ -208,7 +207,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ uint4 Kt[2][NGS];
   __shared__ uint4 Vt[2][NGS];
 
-  const int row = xcd_row(blockIdx.x, total_rows);
+  // position in the processing order -> row (a permutation from the mask builder, which
+  // lists long rows first inside each XCD's range, or the identity)
+  const int pos = xcd_row(blockIdx.x, total_rows);
+  const int row = meta.order ? __builtin_amdgcn_readfirstlane(meta.order[pos]) : pos;
   const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qn = lane & 31, hf = lane >> 5;

@@ -17,7 +17,8 @@
 //                    registers (cross-lane, LDS or in-register exchanges), prefix
 //                    selection, union with forced / static blocks -> bitmask.
 //   static_kernel    one wavefront per row: static pattern bitmask only.
-//   csr_scan_kernel  exclusive scan of per-row counts -> row_ptr.
+//   csr_scan_kernel  exclusive scan of per-row counts -> row_ptr; optionally the
+//                    processing order (long rows first inside each XCD range).
 //   csr_fill_kernel  one wavefront per row: bitmask -> ascending col_idx.
 #include <hip/hip_runtime.h>
 
@@ -404,12 +405,95 @@ __global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__
 // ------------------------------------------------------------------ CSR
 constexpr int kScanThreads = 1024;
 
-// Single workgroup: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].  Each thread owns a
+// Processing order for the attention kernel: inside each XCD's contiguous row range, rows
+// by descending length class, stable in row index, so long rows (text rows, full heads)
+// start first and do not form the tail.  Class of a row with c kept blocks: 0 for c = 0,
+// else 1 + floor(log2 c).  One workgroup of the scan launch per range, beside the one that
+// scans: every thread owns a run of consecutive rows and counts them per class, a
+// workgroup scan per class gives each thread its output slots, and the rows are written
+// in order (deterministic).
+constexpr int kOrderClasses = 12;   // c <= kMaxMaskBlocks = 2^10 -> classes 0..11
+
+__device__ inline int length_class(int c) { return c <= 0 ? 0 : 32 - __clz(c); }
+
+struct OrderScratch {
+  int wsum[kScanThreads / 64][kOrderClasses];
+  int base[kOrderClasses];
+};
+
+__device__ void order_range(const int32_t* __restrict__ count, int32_t* __restrict__ order, int rows,
+                            int x, OrderScratch& sh) {
+  int lo, hi;
+  xcd_range(x, rows, lo, hi);
+  const int n = hi - lo;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int t0 = lo + threadIdx.x * per, t1 = min(t0 + per, hi);
+  int cnt[kOrderClasses];
+#pragma unroll
+  for (int k = 0; k < kOrderClasses; ++k) cnt[k] = 0;
+  for (int i = t0; i < t1; ++i) {
+    const int cl = length_class(count[i]);
+#pragma unroll
+    for (int k = 0; k < kOrderClasses; ++k) cnt[k] += cl == k ? 1 : 0;
+  }
+  // inclusive scan of each class count over the threads of a wavefront, then over waves
+  int incl[kOrderClasses];
+#pragma unroll
+  for (int k = 0; k < kOrderClasses; ++k) {
+    int v = cnt[k];
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(v, off, 64);
+      if (lane >= off) v += u;
+    }
+    incl[k] = v;
+    if (lane == 63) sh.wsum[wv][k] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kOrderClasses) {   // exclusive wave offsets and class totals
+    const int k = threadIdx.x;
+    int run = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int v = sh.wsum[w][k];
+      sh.wsum[w][k] = run;
+      run += v;
+    }
+    sh.base[k] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {   // class starts, longest class first
+    int start = 0;
+    for (int k = kOrderClasses - 1; k >= 0; --k) {
+      const int tot = sh.base[k];
+      sh.base[k] = start;
+      start += tot;
+    }
+  }
+  __syncthreads();
+  int slot[kOrderClasses];
+#pragma unroll
+  for (int k = 0; k < kOrderClasses; ++k) slot[k] = lo + sh.base[k] + sh.wsum[wv][k] + incl[k] - cnt[k];
+  for (int i = t0; i < t1; ++i) {
+    const int cl = length_class(count[i]);
+#pragma unroll
+    for (int k = 0; k < kOrderClasses; ++k) {
+      if (cl == k) order[slot[k]++] = i;
+    }
+  }
+}
+
+// Workgroup 0: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].  Each thread owns a
 // run of consecutive rows; one wave-level scan of the per-thread totals.
 __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* __restrict__ count,
                                                                 int32_t* __restrict__ row_ptr,
+                                                                int32_t* __restrict__ order,
                                                                 int rows) {
   __shared__ int wsum[kScanThreads / 64];
+  __shared__ OrderScratch osh;
+  if (blockIdx.x > 0) {   // workgroups 1..8: the processing order of one XCD range each
+    order_range(count, order, rows, blockIdx.x - 1, osh);
+    return;
+  }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int per = (rows + kScanThreads - 1) / kScanThreads;
   const int t0 = threadIdx.x * per;
@@ -535,9 +619,11 @@ hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const M
 }
 
 hipError_t launch_csr(const MaskGeom& g, const MaskWorkspace& ws, int32_t* row_ptr,
-                      int32_t* col_idx, hipStream_t s) {
+                      int32_t* col_idx, int32_t* order, hipStream_t s) {
   const int rows = g.B * g.H * g.Nb;
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, ws.count, row_ptr, rows);
+  // workgroup 0 scans the counts; with an order, workgroups 1..8 order one XCD range each
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(order ? 1 + kXcds : 1), dim3(kScanThreads), 0, s, ws.count,
+                     row_ptr, order, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, ws.bits,

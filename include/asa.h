@@ -93,14 +93,28 @@ typedef struct asa_head_pattern {
 /* Block mask in CSR form: one row per (b, h, query block r), rows in [B, H, Nb] order.
  * row_ptr has B*H*Nb + 1 entries (row_ptr[0] = 0, row_ptr[last] = number of kept tiles);
  * col_idx lists the kept key blocks of each row in ascending order.  Both are device
- * int32 arrays owned by the caller; capacity is the length of col_idx in elements. */
+ * int32 arrays owned by the caller; capacity is the length of col_idx in elements.
+ *
+ * order (optional, may be NULL) is the attention schedule: a device int32 array of
+ * B*H*Nb entries holding a permutation of the rows.  The pages leave the work order open;
+ * this schedule exists for load balance.  It splits the rows into 8 contiguous ranges,
+ * one per XCD of the MI355X (range x starts at
+ * x*floor(R/8) + min(x, R%8) for R rows, and the first R%8 ranges hold one extra row).
+ *   - asa_build_mask / asa_static_mask fill it when non-NULL.  Inside each range the rows
+ *     come longest first: by length class (0 for an empty row, else 1 + floor(log2 of
+ *     the kept count)) descending, ties in row order.  The result is deterministic.
+ *   - asa_attention_fwd processes the rows in this order when it is non-NULL, and in row
+ *     order otherwise.  The outputs are bit-identical either way.  A caller-made order
+ *     must be a permutation of 0..B*H*Nb-1 that keeps every row inside its range, or rows
+ *     go unwritten (not checked: the array is device memory). */
 typedef struct asa_csr {
   int32_t* row_ptr;
   int32_t* col_idx;
   int64_t capacity;
+  int32_t* order;
 } asa_csr;
 
-/* Library version (major*10000 + minor*100 + patch). */
+/* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */
