@@ -22,9 +22,14 @@ What it computes, in the order the method applies it:
   whose probability mass reaches tau, optionally capped), plus the diagonal
   block and any block holding text tokens.
 
+* Backward of the masked attention -- the gradients (dQ, dK, dV) of
+  sum(dO * O) by the chain rule through each row softmax, and the log of each
+  row's softmax normaliser (what a training forward keeps for the backward).
+  BLADE trains the sparse attention jointly with step distillation (abstract).
+
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
-against closed forms, library routines (torch SDPA, scipy softmax) and brute
-force.  The pooled-score rule and the tuned top-k are specification choices:
+against closed forms, library routines (torch SDPA and its autograd, scipy
+softmax / logsumexp), finite differences and brute force.  The pooled-score rule and the tuned top-k are specification choices:
 their fidelity to BLADE's own ASA is parity unpinned (the pages do not state
 it).
 
@@ -343,3 +348,96 @@ def kept_tile_flops(M: np.ndarray, N: int, blk: int, d: int) -> float:
                       for c in range(Nb)], dtype=np.float64)
     per_tile = 4.0 * np.outer(sizes, sizes) * d
     return float((M * per_tile).sum())
+
+
+# ---------------------------------------------------------------------------- backward
+# Gradients of the masked attention above.  BLADE ("BLADE: Block-Sparse Attention Meets
+# Step Distillation for Efficient Video Generation", abstract) trains the sparse attention
+# jointly with step distillation, so training needs the gradient through the same masked
+# attention (Sparse-vDiT, section 三 "核心公式").  Derived by the chain rule through
+# the row softmax of each query row, over the same kept token set J_i as the forward:
+#   s = q k^T / sqrt(d),  P = softmax(s) per row,  O = P v
+#   dv = P^T dO,  dP = dO v^T,  ds = P * (dP - rowsum(P * dP)),
+#   dq = ds k / sqrt(d),  dk = ds^T q / sqrt(d).
+# Query rows with no kept token have O = 0 and get dq = 0; they add nothing to dk, dv.
+
+def attention_lse(Q: np.ndarray, K: np.ndarray, M: np.ndarray, blk: int) -> np.ndarray:
+    """log of the softmax normaliser per query: log sum_{j in J_i} exp(q_i.k_j / sqrt(d)).
+
+    [B, H, N] float64; -inf for queries whose row keeps no block.
+    """
+    B, H, N, d = Q.shape
+    Nb = num_blocks(N, blk)
+    L = np.full((B, H, N), -np.inf, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(Nb):
+                J = kept_tokens(M[b, h, r], N, blk)
+                if J.size == 0:
+                    continue
+                lo, hi = block_range(r, N, blk)
+                s = (Q[b, h, lo:hi].astype(np.float64) @ K[b, h, J].astype(np.float64).T) / np.sqrt(d)
+                mx = s.max(axis=1)
+                L[b, h, lo:hi] = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+    return L
+
+
+def _row_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray):
+    """(dq, dk, dv) of sum(g * softmax(q k^T / sqrt(d)) v) for one set of query rows."""
+    d = q.shape[-1]
+    s = (q @ k.T) / np.sqrt(d)
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    P = e / e.sum(axis=1, keepdims=True)
+    dv = P.T @ g
+    dP = g @ v.T
+    D = (P * dP).sum(axis=1, keepdims=True)
+    ds = P * (dP - D)
+    dq = (ds @ k) / np.sqrt(d)
+    dk = (ds.T @ q) / np.sqrt(d)
+    return dq, dk, dv
+
+
+def attention_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, M: np.ndarray,
+                  blk: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients (dQ, dK, dV) of sum(dO * attention(Q, K, V, M, blk)), float64."""
+    B, H, N, d = Q.shape
+    Nb = num_blocks(N, blk)
+    dQ = np.zeros((B, H, N, d), dtype=np.float64)
+    dK = np.zeros((B, H, N, d), dtype=np.float64)
+    dV = np.zeros((B, H, N, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(Nb):
+                J = kept_tokens(M[b, h, r], N, blk)
+                if J.size == 0:
+                    continue
+                lo, hi = block_range(r, N, blk)
+                dq, dk, dv = _row_attention_bwd(
+                    Q[b, h, lo:hi].astype(np.float64), K[b, h, J].astype(np.float64),
+                    V[b, h, J].astype(np.float64), dO[b, h, lo:hi].astype(np.float64))
+                dQ[b, h, lo:hi] = dq
+                dK[b, h, J] += dk
+                dV[b, h, J] += dv
+    return dQ, dK, dV
+
+
+def attention_bwd_block(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, M: np.ndarray,
+                        blk: int, b: int, h: int, r: int):
+    """dQ of the query tokens of block r of head (b, h), and that row's contributions to dK
+    and dV as (tokens J, dk [|J|, d], dv [|J|, d])."""
+    N, d = Q.shape[2], Q.shape[3]
+    lo, hi = block_range(r, N, blk)
+    J = kept_tokens(M[b, h, r], N, blk)
+    if J.size == 0:
+        z = np.zeros((0, d), dtype=np.float64)
+        return np.zeros((hi - lo, d), dtype=np.float64), J, z, z
+    dq, dk, dv = _row_attention_bwd(Q[b, h, lo:hi].astype(np.float64), K[b, h, J].astype(np.float64),
+                                    V[b, h, J].astype(np.float64), dO[b, h, lo:hi].astype(np.float64))
+    return dq, J, dk, dv
+
+
+def attention_bwd_flops(M: np.ndarray, N: int, blk: int, d: int) -> float:
+    """Algorithmic backward flops: sum over kept tiles of 10 * n_r * n_c * d (the five
+    products s, dP, dv, dq, dk at 2 flops per multiply-add)."""
+    return 2.5 * kept_tile_flops(M, N, blk, d)

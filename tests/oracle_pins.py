@@ -292,6 +292,111 @@ def check_kept_tile_flops():
     assert O.kept_tile_flops(M, N, blk, d) == 4.0 * pairs * d
 
 
+# ------------------------------------------------------------------ backward pins
+def _token_mask(M, N, blk):
+    """Block mask [B,H,Nb,Nb] -> token mask [B,H,N,N] (True = the pair is attended)."""
+    idx = np.arange(N) // blk
+    return M[:, :, idx][:, :, :, idx]
+
+
+def _masked_loss(q, k, v, M, blk, g):
+    return float((O.attention(q, k, v, M, blk) * g).sum())
+
+
+def check_bwd_finite_differences():
+    """dQ, dK, dV against central differences of sum(G * O) (ragged N, an empty row)."""
+    B, H, N, d, blk = 1, 2, 40, 8, 16
+    q, k, v = _qkv(B, H, N, d, 31)
+    g = RNG(32).standard_normal((B, H, N, d))
+    Nb = O.num_blocks(N, blk)
+    M = RNG(33).random((B, H, Nb, Nb)) < 0.6
+    M[0, 0, 0] = [True, False, True]
+    M[0, 1, 1] = False                      # a query block with no kept key block
+    dq, dk, dv = O.attention_bwd(q, k, v, g, M, blk)
+    eps = 1e-5
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.empty_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = _masked_loss(q, k, v, M, blk, g)
+            x[i] = old - eps
+            lm = _masked_loss(q, k, v, M, blk, g)
+            x[i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        assert np.allclose(grad, fd, atol=1e-7, rtol=1e-6), (name, np.abs(grad - fd).max())
+
+
+def check_bwd_matches_torch_autograd():
+    """Gradients of torch SDPA (float64, token-level boolean mask) through autograd."""
+    B, H, N, d, blk = 1, 3, 200, 16, 64
+    q, k, v = _qkv(B, H, N, d, 34)
+    g = RNG(35).standard_normal((B, H, N, d))
+    Nb = O.num_blocks(N, blk)
+    M = RNG(36).random((B, H, Nb, Nb)) < 0.5
+    M[..., np.arange(Nb), np.arange(Nb)] = True   # every row attends somewhere (SDPA needs it)
+    t = [torch.from_numpy(np.ascontiguousarray(x)).requires_grad_(True) for x in (q, k, v)]
+    mask = torch.from_numpy(_token_mask(M, N, blk))
+    out = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=mask)
+    (out * torch.from_numpy(g)).sum().backward()
+    dq, dk, dv = O.attention_bwd(q, k, v, g, M, blk)
+    for mine, ref in ((dq, t[0].grad), (dk, t[1].grad), (dv, t[2].grad)):
+        assert np.allclose(mine, ref.numpy(), atol=1e-11, rtol=0)
+
+
+def check_bwd_identical_keys_closed_form():
+    """One kept block of identical keys: P is uniform, so dQ = 0 and dV_j = mean_i G_i."""
+    B, H, N, d, blk = 1, 1, 96, 8, 32
+    q, k, v = _qkv(B, H, N, d, 37)
+    k[0, 0, 32:64] = k[0, 0, 40]            # key block 1: one repeated key
+    g = RNG(38).standard_normal((B, H, N, d))
+    M = np.zeros((B, H, 3, 3), dtype=bool)
+    M[0, 0, 0, 1] = True                     # query block 0 attends key block 1 only
+    dq, dk, dv = O.attention_bwd(q, k, v, g, M, blk)
+    assert np.allclose(dq[0, 0, :32], 0.0, atol=1e-12)
+    assert np.allclose(dv[0, 0, 32:64], np.broadcast_to(g[0, 0, :32].mean(axis=0), (32, d)), atol=1e-12)
+    assert np.all(dq[0, 0, 32:] == 0) and np.all(dk[0, 0, :32] == 0) and np.all(dv[0, 0, 64:] == 0)
+
+
+def check_bwd_blocks_assemble_full():
+    """Per-row pieces (attention_bwd_block) add up to the whole-tensor gradients."""
+    B, H, N, d, blk = 1, 2, 100, 8, 32
+    q, k, v = _qkv(B, H, N, d, 39)
+    g = RNG(40).standard_normal((B, H, N, d))
+    Nb = O.num_blocks(N, blk)
+    M = RNG(41).random((B, H, Nb, Nb)) < 0.5
+    dq, dk, dv = O.attention_bwd(q, k, v, g, M, blk)
+    dq2, dk2, dv2 = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+    for h in range(H):
+        for r in range(Nb):
+            lo, hi = O.block_range(r, N, blk)
+            a, J, bk, bv = O.attention_bwd_block(q, k, v, g, M, blk, 0, h, r)
+            dq2[0, h, lo:hi] = a
+            dk2[0, h, J] += bk
+            dv2[0, h, J] += bv
+    assert np.allclose(dq, dq2, atol=1e-13) and np.allclose(dk, dk2, atol=1e-13)
+    assert np.allclose(dv, dv2, atol=1e-13)
+
+
+def check_lse_matches_scipy():
+    """attention_lse == scipy logsumexp of the masked token scores; -inf for empty rows."""
+    B, H, N, d, blk = 1, 2, 90, 8, 32
+    q, k, _ = _qkv(B, H, N, d, 42)
+    Nb = O.num_blocks(N, blk)
+    M = RNG(43).random((B, H, Nb, Nb)) < 0.5
+    M[0, 1, 2] = False
+    L = O.attention_lse(q, k, M, blk)
+    tm = _token_mask(M, N, blk)
+    for h in range(H):
+        s = q[0, h] @ k[0, h].T / math.sqrt(d)
+        s = np.where(tm[0, h], s, -np.inf)
+        ref = scipy.special.logsumexp(s, axis=1)
+        assert np.allclose(L[0, h], ref, atol=1e-12, rtol=0, equal_nan=False)
+    assert np.all(np.isneginf(L[0, 1, 64:]))
+
+
 ALL_CHECKS = [
     check_dense_equals_sdpa, check_block_diagonal_equals_independent_blocks,
     check_weights_sum_to_one, check_identical_keys_give_mean_of_v,
@@ -301,4 +406,6 @@ ALL_CHECKS = [
     check_selection_limits_and_monotone, check_forced_blocks,
     check_static_patterns_token_pairs, check_static_counts_8192, check_csr_layout,
     check_kept_tile_flops,
+    check_bwd_finite_differences, check_bwd_matches_torch_autograd,
+    check_bwd_identical_keys_closed_form, check_bwd_blocks_assemble_full, check_lse_matches_scipy,
 ]

@@ -94,6 +94,30 @@ def _row_attention_no_normalise(q, k, v):
     return e @ v
 
 
+def _bwd_variant(which):
+    def f(q, k, v, g):
+        d = q.shape[-1]
+        s_ = (q @ k.T) / np.sqrt(d)
+        e = np.exp(s_ - s_.max(axis=1, keepdims=True))
+        P = e / e.sum(axis=1, keepdims=True)
+        dv = (e.T @ g) if which == "dv_unnormalised" else P.T @ g
+        dP = g @ v.T
+        D = (P * dP).sum(axis=1, keepdims=True)
+        ds = P * dP if which == "ds_missing_rowsum" else P * (dP - D)
+        dq = (ds @ (v if which == "dq_uses_v" else k)) / np.sqrt(d)
+        dk = (ds.T @ q) if which == "dk_missing_scale" else (ds.T @ q) / np.sqrt(d)
+        return dq, dk, dv
+    return f
+
+
+_orig_lse = core.attention_lse
+
+
+def _lse_unscaled(Q, K, M, blk):
+    B, H, N, d = Q.shape
+    return _orig_lse(Q * np.sqrt(d), K, M, blk)
+
+
 MUTATIONS = {
     "pool_sum_not_mean": ("pool", _pool_sum),
     "pool_zero_padded_partial_block": ("pool", _pool_zero_padded),
@@ -105,6 +129,11 @@ MUTATIONS = {
     "attention_drops_partial_key_block": ("kept_tokens", _kept_tokens_full_blocks_only),
     "multidiag_floor_not_ceiling": ("static_row", _static_floor),
     "attention_not_normalised": ("_row_attention", _row_attention_no_normalise),
+    "bwd_dk_missing_scale": ("_row_attention_bwd", _bwd_variant("dk_missing_scale")),
+    "bwd_ds_missing_rowsum": ("_row_attention_bwd", _bwd_variant("ds_missing_rowsum")),
+    "bwd_dq_uses_v": ("_row_attention_bwd", _bwd_variant("dq_uses_v")),
+    "bwd_dv_unnormalised": ("_row_attention_bwd", _bwd_variant("dv_unnormalised")),
+    "lse_missing_scale": ("attention_lse", _lse_unscaled),
 }
 
 
