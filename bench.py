@@ -105,6 +105,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) timing")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -191,6 +192,37 @@ def main():
         result_extra["dense_attn_ms"] = round(dense_ms, 4)
         result_extra["dense_attn_tflops"] = round(dense_flops / dense_ms / 1e9, 2)
         del dout, drp, dci
+
+    if not args.no_bwd:
+        # training path on the same mask: forward keeping lse, then the backward
+        log("bench: backward (forward with lse, then dQ, dK, dV)")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], row_ptr, col_idx, blk, order=order, lse=lse, out=out)
+        g = torch.from_numpy(np.random.default_rng(5).standard_normal((B, H, N, d)).astype(np.float32))
+        gout = g.to(torch.bfloat16).to(dev)
+        grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+        bws = torch.empty(int(asa.lib.asa_attention_bwd_workspace_size(ctypes.byref(shp))), dtype=torch.uint8,
+                          device=dev)
+
+        def backward():
+            asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], out, gout, lse, row_ptr, col_idx, blk,
+                                  grads=grads, workspace=bws)
+
+        for _ in range(3):
+            backward()
+        torch.cuda.synchronize()
+        nb = 10
+        bev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        bev[0].record(stream)
+        for _ in range(nb):
+            backward()
+        bev[1].record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = bev[0].elapsed_time(bev[1]) / nb
+        result_extra["bwd_ms"] = round(bwd_ms, 4)
+        # five products per kept tile (S, dP, dV, dK, dQ): 2.5x the forward's flops
+        result_extra["bwd_tflops"] = round(2.5 * flops / bwd_ms / 1e9, 2)
+        del gout, grads, bws, lse
 
     attn_tflops = flops / attn_ms / 1e9
     mask_bytes = 2.0 * B * H * N * d * 2 + 4.0 * (rows + 1 + kept)   # Q, K read once; CSR written

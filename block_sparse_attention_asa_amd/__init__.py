@@ -59,15 +59,29 @@ EXPORTS = {
     "asa_attention_fwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.POINTER(asa_shape), ctypes.POINTER(asa_csr),
                                          ctypes.POINTER(asa_head_pattern), ctypes.c_float, ctypes.c_void_p]),
+    "asa_attention_fwd_lse": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.POINTER(asa_shape), ctypes.POINTER(asa_csr),
+                                             ctypes.POINTER(asa_head_pattern), ctypes.c_float, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
+    "asa_attention_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(asa_shape)]),
+    "asa_attention_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(asa_shape),
+                                         ctypes.POINTER(asa_csr), ctypes.POINTER(asa_head_pattern),
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_sparse_attention_asa_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python block_sparse_attention_asa_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in EXPORTS.items():
-        fn = getattr(lib, name)
+        try:
+            fn = getattr(lib, name)
+        except AttributeError:
+            raise ImportError(f"{LIB_PATH} does not export {name} (built from older sources); "
+                              f"run `python block_sparse_attention_asa_amd/build.py`") from None
         fn.restype = res
         fn.argtypes = args
     return lib
@@ -225,12 +239,13 @@ def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr
                       col_idx: torch.Tensor, blk: int, *,
                       patterns: Optional[Sequence[Tuple[int, int]]] = None,
                       out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
-                      order: Optional[torch.Tensor] = None,
+                      order: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Block-sparse attention over the kept tiles of the CSR mask; returns O [B,H,N,d].
 
     `order`, from a mask builder's with_order, sets the processing order of the rows; the
-    result does not depend on it.
+    result does not depend on it.  `lse` (float32 [B,H,N]), if given, receives the log of
+    each query's softmax normaliser (what asa_attention_bwd needs).
     """
     _require_device(q, k, v, row_ptr, col_idx)
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
@@ -251,12 +266,61 @@ def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr
             raise ValueError("order must be int32 with one entry per CSR row")
     csr = _csr_struct(row_ptr, col_idx, order)
     pats = _patterns(patterns, H)
-    _check(lib.asa_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), o_code,
-                                 ctypes.byref(shp), ctypes.byref(csr), pats, float(scale),
-                                 _stream(q.device, stream)), "asa_attention_fwd")
+    if lse is None:
+        _check(lib.asa_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), o_code,
+                                     ctypes.byref(shp), ctypes.byref(csr), pats, float(scale),
+                                     _stream(q.device, stream)), "asa_attention_fwd")
+    else:
+        _require_device(lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be float32 [B, H, N]")
+        _check(lib.asa_attention_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), o_code,
+                                         ctypes.byref(shp), ctypes.byref(csr), pats, float(scale),
+                                         lse.data_ptr(), _stream(q.device, stream)), "asa_attention_fwd_lse")
     return out
 
 
-__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_csr_capacity",
+def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                      dout: torch.Tensor, lse: torch.Tensor, row_ptr: torch.Tensor,
+                      col_idx: torch.Tensor, blk: int, *,
+                      patterns: Optional[Sequence[Tuple[int, int]]] = None, scale: float = 0.0,
+                      grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dQ, dK, dV), float32 [B,H,N,d], of sum(dout * O) for the block-sparse
+    attention O = asa_attention_fwd(q, k, v, row_ptr, col_idx, blk) with its `lse`."""
+    _require_device(q, k, v, o, dout, lse, row_ptr, col_idx)
+    if not (q.shape == k.shape == v.shape == o.shape == dout.shape):
+        raise ValueError("q, k, v, o and dout must share one shape")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype == torch.bfloat16):
+        raise ValueError("the backward takes bfloat16 q, k, v and dout")
+    shp = _shape_of(q, blk)
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    if row_ptr.numel() != B * H * num_blocks(N, blk) + 1:
+        raise ValueError("row_ptr length does not match [B, H, Nb] rows")
+    if grads is None:
+        grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) for _ in range(3))
+    dq, dk, dv = grads
+    _require_device(dq, dk, dv)
+    for g in grads:
+        if g.dtype != torch.float32 or g.shape != q.shape:
+            raise ValueError("gradients are float32 with the shape of q")
+    need = int(lib.asa_attention_bwd_workspace_size(ctypes.byref(shp)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    csr = _csr_struct(row_ptr, col_idx, None)
+    pats = _patterns(patterns, H)
+    _check(lib.asa_attention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o),
+                                 dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 ctypes.byref(shp), ctypes.byref(csr), pats, float(scale),
+                                 workspace.data_ptr(), workspace.numel(), _stream(q.device, stream)),
+           "asa_attention_bwd")
+    return dq, dk, dv
+
+
+__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attention_bwd", "asa_csr_capacity",
            "AsaError", "lib", "LIB_PATH", "EXPORTS", "num_blocks",
            "ADAPTIVE", "FULL", "SKIP", "DIAG", "MULTIDIAG", "VSTRIPE", "TOPK", "TAU"]

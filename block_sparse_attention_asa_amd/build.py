@@ -1,6 +1,7 @@
 """Build libasa.so (the C-ABI library with its gfx950 kernels) in-tree with hipcc.
 
-Usage: python -m block_sparse_attention_asa_amd.build  [--verbose]
+Usage: python block_sparse_attention_asa_amd/build.py  [--verbose]
+(run by path: importing the package loads the library, which may not be built yet)
 Output: block_sparse_attention_asa_amd/libasa.so
 """
 import os
@@ -17,7 +18,7 @@ LIB = os.path.join(PKG, "libasa.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["asa_api.cpp", "mask.hip", "attn_fwd.hip"]
+SOURCES = ["asa_api.cpp", "mask.hip", "attn_fwd.hip", "attn_bwd.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

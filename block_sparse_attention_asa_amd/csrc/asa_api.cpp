@@ -215,10 +215,12 @@ asa_status asa_static_mask(const asa_shape* shape, const asa_head_pattern* patte
   return ASA_OK;
 }
 
-asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* O, int32_t o_dtype,
-                             const asa_shape* shape, const asa_csr* csr,
-                             const asa_head_pattern* patterns, float scale, void* stream) {
+static asa_status attention_fwd_impl(const void* Q, const void* K, const void* V, void* O,
+                                     int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
+                                     const asa_head_pattern* patterns, float scale, float* lse,
+                                     bool need_lse, void* stream) {
   g_last_error[0] = '\0';
+  if (need_lse && !lse) return fail(ASA_ERR_NULL_ARG, "lse is NULL");
   asa_status st = check_shape(shape, false);
   if (st != ASA_OK) return st;
   if (!Q || !K || !V || !O) return fail(ASA_ERR_NULL_ARG, "Q, K, V or O is NULL");
@@ -235,6 +237,7 @@ asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* 
   a.row_ptr = csr->row_ptr;
   a.col_idx = csr->col_idx;
   a.order = csr->order;
+  a.lse = lse;
   a.B = shape->B; a.H = shape->H; a.N = shape->N; a.d = shape->d; a.blk = shape->blk;
   a.Nb = (int)num_blocks(shape);
   a.in_bf16 = shape->in_dtype == ASA_BF16;
@@ -246,6 +249,68 @@ asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* 
       if (patterns[h].id == ASA_PAT_SKIP) a.skip_bits[h >> 5] |= 1u << (h & 31);
   hipError_t e = asa::launch_attention(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention");
+  return ASA_OK;
+}
+
+asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* O, int32_t o_dtype,
+                             const asa_shape* shape, const asa_csr* csr,
+                             const asa_head_pattern* patterns, float scale, void* stream) {
+  return attention_fwd_impl(Q, K, V, O, o_dtype, shape, csr, patterns, scale, nullptr, false, stream);
+}
+
+asa_status asa_attention_fwd_lse(const void* Q, const void* K, const void* V, void* O, int32_t o_dtype,
+                                 const asa_shape* shape, const asa_csr* csr,
+                                 const asa_head_pattern* patterns, float scale, float* lse,
+                                 void* stream) {
+  return attention_fwd_impl(Q, K, V, O, o_dtype, shape, csr, patterns, scale, lse, true, stream);
+}
+
+size_t asa_attention_bwd_workspace_size(const asa_shape* shape) {
+  if (check_shape(shape, true) != ASA_OK) return 0;
+  asa::BwdArgs g{};
+  g.B = shape->B; g.H = shape->H; g.N = shape->N; g.d = shape->d; g.blk = shape->blk;
+  g.Nb = (int)num_blocks(shape);
+  return asa::bwd_workspace_layout(g, nullptr, nullptr);
+}
+
+asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const void* O,
+                             int32_t o_dtype, const void* dO, const float* lse, float* dQ, float* dK,
+                             float* dV, const asa_shape* shape, const asa_csr* csr,
+                             const asa_head_pattern* patterns, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  asa_status st = check_shape(shape, true);
+  if (st != ASA_OK) return st;
+  if (shape->in_dtype != ASA_BF16)
+    return fail(ASA_ERR_UNSUPPORTED, "the backward takes ASA_BF16 inputs (in_dtype=%d)", shape->in_dtype);
+  if (!Q || !K || !V || !O || !dO || !lse) return fail(ASA_ERR_NULL_ARG, "Q, K, V, O, dO or lse is NULL");
+  if (!dQ || !dK || !dV) return fail(ASA_ERR_NULL_ARG, "dQ, dK or dV is NULL");
+  if (o_dtype != ASA_F32 && o_dtype != ASA_BF16)
+    return fail(ASA_ERR_BAD_DTYPE, "o_dtype=%d is not ASA_F32 or ASA_BF16", o_dtype);
+  if (!csr) return fail(ASA_ERR_NULL_ARG, "csr is NULL");
+  if (!csr->row_ptr || !csr->col_idx) return fail(ASA_ERR_NULL_ARG, "csr row_ptr/col_idx is NULL");
+  if (!(std::isfinite(scale))) return fail(ASA_ERR_BAD_PARAM, "scale must be finite");
+  asa::HeadTable heads;
+  if ((st = fill_heads(shape, patterns, true, &heads)) != ASA_OK) return st;
+  asa::BwdArgs a{};
+  a.B = shape->B; a.H = shape->H; a.N = shape->N; a.d = shape->d; a.blk = shape->blk;
+  a.Nb = (int)num_blocks(shape);
+  const size_t need = asa::bwd_workspace_layout(a, nullptr, nullptr);
+  if ((st = check_workspace(workspace, workspace_bytes, need)) != ASA_OK) return st;
+  asa::bwd_workspace_layout(a, &a, workspace);
+  a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = lse;
+  a.dq = dQ; a.dk = dK; a.dv = dV;
+  a.row_ptr = csr->row_ptr;
+  a.col_idx = csr->col_idx;
+  a.o_bf16 = o_dtype == ASA_BF16;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)shape->d);
+  a.scale = (float)sc;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  if (patterns)
+    for (int h = 0; h < shape->H; ++h)
+      if (patterns[h].id == ASA_PAT_SKIP) a.skip_bits[h >> 5] |= 1u << (h & 31);
+  hipError_t e = asa::launch_attention_bwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention backward");
   return ASA_OK;
 }
 

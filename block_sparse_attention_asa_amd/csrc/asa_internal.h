@@ -67,6 +67,7 @@ struct AttnArgs {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const int32_t* order;  // processing order of the rows, or NULL for row order
+  float* lse;            // [B,H,N] log of each query's softmax normaliser, or NULL
   int32_t B, H, N, d, blk, Nb;
   bool in_bf16, out_bf16;
   float scale_log2;      // softmax scale times log2(e)
@@ -74,5 +75,32 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// Attention backward (bf16 inputs, fp32 gradients).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;        // [B,H,N] natural-log softmax normaliser from the forward
+  float* dq;
+  float* dk;
+  float* dv;
+  const int32_t* row_ptr;  // CSR mask
+  const int32_t* col_idx;
+  int32_t* col_ptr;        // transposed mask (workspace): [B*H*Nb + 1]
+  int32_t* row_idx;        // [B*H*Nb*Nb] capacity, query blocks ascending per key block
+  float* ld;               // [B*H*N][2] (lse * log2(e), D = dO . O) per query (workspace)
+  int32_t B, H, N, d, blk, Nb;
+  bool o_bf16;
+  float scale;             // softmax scale
+  float scale_log2;        // scale * log2(e)
+  uint32_t skip_bits[kMaxHeads / 32];
+};
+
+// Workspace carve-up for the backward; returns the bytes needed (base may be NULL).
+size_t bwd_workspace_layout(const BwdArgs& geom, BwdArgs* a, void* base);
+hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t s);
 
 }  // namespace asa

@@ -1,0 +1,593 @@
+// Block-sparse attention backward for gfx950 (MI355X), bf16 inputs, fp32 gradients.
+//
+// The gradients of the masked attention of Sparse-vDiT ("Sparse-vDiT: Sparse Attention
+// Acceleration for Video Diffusion Transformers", section 三 "核心公式"); BLADE
+// ("BLADE: Block-Sparse Attention Meets Step Distillation for Efficient Video
+// Generation", abstract) trains the sparse attention jointly with distillation.  With
+// P_ij = exp(scale Q_i.K_j - lse_i) over the kept tokens j of query i's row:
+//     dV_j = sum_i P_ij dO_i        dP_ij = dO_i . V_j        D_i = dO_i . O_i
+//     dS_ij = P_ij (dP_ij - D_i)    dQ_i = scale sum_j dS_ij K_j
+//     dK_j = scale sum_i dS_ij Q_i
+// The weights are recomputed from Q, K and the forward's lse, so nothing of size N x N
+// is stored.
+//
+// Kernels (all on the caller's stream):
+//   bwd_prep_kernel  per query: (lse * log2 e, D = dO . O) -> workspace pairs.
+//   csc_kernel       one workgroup per head: CSR -> CSC (key block -> query blocks in
+//                    ascending order) through a transposed bitmask in LDS.
+//   dq_kernel        one workgroup per query-block row, like the forward: K and V of every
+//                    kept key block stream through an LDS ring; per 64-key step
+//                    S^T = K Q^T, P^T = exp2(S^T s - lse), dP^T = V dO^T,
+//                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T  (K^T by transpose reads).
+//   dkv_kernel       one workgroup per key block (32 keys per wavefront: their K in
+//                    registers, their V in lane-private LDS); Q, dO and the (lse, D) pairs
+//                    of every query block that
+//                    keeps it stream through an LDS ring; per 32-query step
+//                    S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
+// Each gradient element is accumulated by one lane in a fixed order (no atomics), so the
+// results are deterministic.
+#include <hip/hip_runtime.h>
+
+#include "attn_common.h"
+
+namespace asa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ preprocessing
+// TPQ = D/8 consecutive threads per query, 8 elements each; D reduced with shuffles.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ dout,
+                                                       const TO* __restrict__ o,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ ld, size_t nq) {
+  constexpr int TPQ = D / 8;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t q = gid / TPQ;
+  const int part = (int)(gid % TPQ);
+  float acc = 0.f;
+  if (q < nq) {
+    const uint4 g = *reinterpret_cast<const uint4*>(dout + q * D + part * 8);
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    float ov[8];
+    if constexpr (sizeof(TO) == 4) {
+      const float4 a = *reinterpret_cast<const float4*>(o + q * D + part * 8);
+      const float4 b = *reinterpret_cast<const float4*>(o + q * D + part * 8 + 4);
+      ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+      ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+    } else {
+      const uint4 a = *reinterpret_cast<const uint4*>(o + q * D + part * 8);
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ov[2 * j] = __uint_as_float(aw[j] << 16);
+        ov[2 * j + 1] = __uint_as_float(aw[j] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = __builtin_fmaf(__uint_as_float(gw[j] << 16), ov[2 * j], acc);
+      acc = __builtin_fmaf(__uint_as_float(gw[j] & 0xffff0000u), ov[2 * j + 1], acc);
+    }
+  }
+  for (int off = TPQ / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (q < nq && part == 0) {
+    ld[2 * q] = lse[q] * kLog2e;
+    ld[2 * q + 1] = acc;
+  }
+}
+
+// ------------------------------------------------------------------ CSR -> CSC
+// One workgroup per (b, h).  Bit (c, r) of an LDS bitmask marks "query block r keeps key
+// block c"; column c's list is then read off in ascending r.  The head's CSC segment
+// starts where its CSR segment does (same number of kept tiles).
+constexpr int kCscThreads = 1024;
+__global__ __launch_bounds__(kCscThreads) void csc_kernel(const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx,
+                                                          int32_t* __restrict__ col_ptr,
+                                                          int32_t* __restrict__ row_idx, int Nb,
+                                                          int heads) {
+  __shared__ uint32_t bitT[kMaxMaskBlocks * (kMaxMaskBlocks / 32)];
+  __shared__ int wsum[kCscThreads / 64];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int words = (Nb + 31) / 32;
+  for (int i = tid; i < Nb * words; i += kCscThreads) bitT[i] = 0u;
+  __syncthreads();
+  const int rbase = bh * Nb;
+  for (int r = tid; r < Nb; r += kCscThreads) {
+    const int e1 = row_ptr[rbase + r + 1];
+    for (int e = row_ptr[rbase + r]; e < e1; ++e) {
+      const int c = col_idx[e];
+      atomicOr(&bitT[c * words + (r >> 5)], 1u << (r & 31));
+    }
+  }
+  __syncthreads();
+  const int c = tid;   // Nb <= kCscThreads: one key block per thread
+  int cnt = 0;
+  if (c < Nb)
+    for (int w = 0; w < words; ++w) cnt += __popc(bitT[c * words + w]);
+  int incl = cnt;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  if (wv == 0) {
+    const int v0 = lane < kCscThreads / 64 ? wsum[lane] : 0;
+    int x = v0;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(x, off, 64);
+      if (lane >= off) x += v;
+    }
+    if (lane < kCscThreads / 64) wsum[lane] = x - v0;
+  }
+  __syncthreads();
+  if (c < Nb) {
+    int pos = row_ptr[rbase] + wsum[wv] + incl - cnt;
+    col_ptr[rbase + c] = pos;
+    for (int w = 0; w < words; ++w) {
+      uint32_t b = bitT[c * words + w];
+      while (b) {
+        row_idx[pos++] = w * 32 + __ffs(b) - 1;
+        b &= b - 1u;
+      }
+    }
+  }
+  if (bh == heads - 1 && tid == 0) col_ptr[heads * Nb] = row_ptr[heads * Nb];
+}
+
+// V^T-style fragment by transpose reads: rows kbase.. of a row-major swizzled [rows][D]
+// bf16 tile, columns 32*io + ..; element j of lane half hf comes from row
+// 16*u + 8*(j/4) + 4*hf + j%4 (the k order of the MFMA output layout).  Lane s of 16-lane
+// group g supplies row 16u + 8tt + 4(g/2) + s/4, columns dcol.. (4 elements); lane i of the
+// group receives column dcol + i of those four rows.
+template <int D>
+__device__ inline Frag<uint16_t> tr_frag(const uint16_t* tile, int io, int u, int lane) {
+  constexpr int GPR = D * 2 / 16;
+  const int g = lane >> 4, sl = lane & 15;
+  const int dcol = 32 * io + 16 * (g & 1) + 4 * (sl & 3);
+  short4_t part[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
+    const int gran = (dcol >> 3) ^ swz<GPR>(kr);
+    const uint16_t* p = tile + kr * D + gran * 8 + (dcol & 7);
+    part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+  }
+  const uint2 lo = __builtin_bit_cast(uint2, part[0]);
+  const uint2 hi = __builtin_bit_cast(uint2, part[1]);
+  Frag<uint16_t> a;
+  a.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return a;
+}
+
+// Pack 8 fp32 values to one bf16 fragment (round to nearest even).
+__device__ inline Frag<uint16_t> pack_bf16(const float (&x)[8]) {
+  uint32_t wd[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x2_t pk = {static_cast<__bf16>(x[2 * j]), static_cast<__bf16>(x[2 * j + 1])};
+    wd[j] = __builtin_bit_cast(uint32_t, pk);
+  }
+  Frag<uint16_t> f;
+  f.v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  return f;
+}
+
+// Store a transposed [32 x 32*kOut] accumulator (lane = token row, registers = columns)
+// as fp32 rows of D: acc[io][4g + t] is column 32io + 8g + 4hf + t.
+template <int kOut, int D>
+__device__ inline void store_rows(float* row, const f32x16_t (&acc)[kOut], float mul, int hf) {
+#pragma unroll
+  for (int io = 0; io < kOut; ++io)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * io + 8 * g + 4 * hf;
+      *reinterpret_cast<float4*>(row + d0) =
+          make_float4(acc[io][4 * g] * mul, acc[io][4 * g + 1] * mul, acc[io][4 * g + 2] * mul,
+                      acc[io][4 * g + 3] * mul);
+    }
+}
+
+// ------------------------------------------------------------------ dQ over CSR rows
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(BwdArgs a) {
+  using T = uint16_t;
+  constexpr int KT = 64;
+  constexpr int kSteps = BLK / KT;
+  constexpr int kWaves = BLK / 32;
+  constexpr int NT = 64 * kWaves;
+  constexpr int GPR = D * 2 / 16;
+  constexpr int NGS = KT * GPR;
+  constexpr int NLD = NGS / NT;
+  constexpr int kQk = D / 16, kSub = KT / 32, kPv = KT / 16, kOut = D / 32;
+  static_assert(NGS % NT == 0 && BLK % KT == 0, "tile shape");
+
+  __shared__ uint4 Kt[2][NGS];
+  __shared__ uint4 Vt[2][NGS];
+
+  const int N = a.N, Nb = a.Nb, H = a.H;
+  const int total_rows = a.B * H * Nb;
+  const int row = xcd_row(blockIdx.x, total_rows);
+  const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qn = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const int qi = r * BLK + w * 32 + qn;
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  const T* dO = static_cast<const T*>(a.dout);
+
+  const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[row]);
+  int e1 = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]);
+  if ((a.skip_bits[h >> 5] >> (h & 31)) & 1u) e1 = e0;
+
+  f32x16_t acc[kOut];
+#pragma unroll
+  for (int io = 0; io < kOut; ++io) acc[io] = f32x16_t{};
+
+  if (e1 > e0) {
+    Frag<T> qf[kQk], df[kQk];
+    float lse2 = 0.f, dd = 0.f;
+#pragma unroll
+    for (int t = 0; t < kQk; ++t) {
+      if (qi < N) {
+        qf[t] = lds_frag(Q + head + (size_t)qi * D + 16 * t + 8 * hf);
+        df[t] = lds_frag(dO + head + (size_t)qi * D + 16 * t + 8 * hf);
+      } else {
+        qf[t] = Frag<T>{};
+        df[t] = Frag<T>{};
+      }
+    }
+    if (qi < N) {
+      const float2 p = *reinterpret_cast<const float2*>(a.ld + 2 * ((size_t)bh * N + qi));
+      lse2 = p.x;
+      dd = p.y;
+    }
+    const uint32_t wave_off = (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
+    const uint32_t k_lds[2] = {lds_addr(Kt[0]) + wave_off, lds_addr(Kt[1]) + wave_off};
+    const uint32_t v_lds[2] = {lds_addr(Vt[0]) + wave_off, lds_addr(Vt[1]) + wave_off};
+    uint32_t off[NLD];
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) off[it] = dma_offset<T, D, NT>(it, tid, KT);
+    auto dma_step = [&](const T* ksrc, const T* vsrc, int slot, int nv) {
+      if (nv == KT) {
+        static_for<NLD>([&](auto it) {
+          dma16<it.value * NT * 16>(ksrc, off[it.value], k_lds[slot]);
+          dma16<it.value * NT * 16>(vsrc, off[it.value], v_lds[slot]);
+        });
+      } else {
+        static_for<NLD>([&](auto it) {
+          const uint32_t o = dma_offset<T, D, NT>(it.value, tid, nv);
+          dma16<it.value * NT * 16>(ksrc, o, k_lds[slot]);
+          dma16<it.value * NT * 16>(vsrc, o, v_lds[slot]);
+        });
+      }
+    };
+    int cbase = e0;
+    int cvec = e0 + lane < e1 ? a.col_idx[e0 + lane] : 0;
+    // the query, dO, (lse, D) and index loads above are done before any transfer: the
+    // compiler does not see the transfers and would otherwise wait on them in the loop
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    int e = e0, hh = 0;
+    int c = __builtin_amdgcn_readlane(cvec, 0);
+    int nkv = min(BLK, N - c * BLK);
+    int slot = 0;
+    {
+      const size_t src = head + (size_t)c * BLK * D;
+      dma_step(K + src, V + src, 0, min(KT, nkv));
+    }
+    for (;;) {
+      int e_n = e, hh_n = hh + 1, c_n = c, nkv_n = nkv;
+      if (hh_n >= kSteps || hh_n * KT >= nkv) {
+        e_n = e + 1;
+        hh_n = 0;
+        if (e_n < e1) {
+          if (e_n - cbase == 64) {
+            cbase += 64;
+            cvec = cbase + lane < e1 ? a.col_idx[cbase + lane] : 0;
+          }
+          c_n = __builtin_amdgcn_readlane(cvec, e_n - cbase);
+          nkv_n = min(BLK, N - c_n * BLK);
+        }
+      }
+      const bool more = e_n < e1;
+      const int nv = min(KT, nkv - hh * KT);
+
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wg_barrier();
+      if (more) {
+        const size_t src = head + ((size_t)c_n * BLK + hh_n * KT) * D;
+        dma_step(K + src, V + src, slot ^ 1, min(KT, nkv_n - hh_n * KT));
+      }
+      const uint4* kt = Kt[slot];
+      const uint4* vt = Vt[slot];
+
+      // per 32-key subtile: S^T = K Q^T and dP^T = V dO^T (keys on rows, this lane's
+      // query on the column), then P^T = exp2(S^T scale log2e - lse log2e) (keys past nv
+      // weigh 0) and dS^T = P^T (dP^T - D), rounded to bf16 for the MFMA
+      Frag<T> dsf[kPv];
+#pragma unroll
+      for (int is = 0; is < kSub; ++is) {
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+        const int kr = 32 * is + qn;
+#pragma unroll
+        for (int t = 0; t < kQk; ++t) {
+          Frag<T> ka, va;
+          ka.v = kt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
+          va.v = vt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
+          mma_k16(s, ka, qf[t]);
+          mma_k16(dp, va, df[t]);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int i = 8 * h2 + j;
+            const int key = 32 * is + 8 * (i >> 2) + 4 * hf + (i & 3);
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -lse2));
+            if (nv < KT && key >= nv) p = 0.f;
+            x[j] = p * (dp[i] - dd);
+          }
+          dsf[2 * is + h2] = pack_bf16(x);
+        }
+      }
+      // dQ^T += K^T dS^T (K^T fragments by transpose reads of the K tile)
+      const uint16_t* ktile = reinterpret_cast<const uint16_t*>(kt);
+#pragma unroll
+      for (int io = 0; io < kOut; ++io)
+#pragma unroll
+        for (int u = 0; u < kPv; ++u) mma_k16(acc[io], tr_frag<D>(ktile, io, u, lane), dsf[u]);
+
+      if (!more) break;
+      e = e_n;
+      hh = hh_n;
+      c = c_n;
+      nkv = nkv_n;
+      slot ^= 1;
+    }
+  }
+  if (qi < N) store_rows<kOut, D>(a.dq + head + (size_t)qi * D, acc, a.scale, hf);
+}
+
+// ------------------------------------------------------------------ dK, dV over CSC
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void dkv_kernel(BwdArgs a) {
+  using T = uint16_t;
+  constexpr int QT = 32;                 // queries per step
+  constexpr int kSteps = BLK / QT;       // steps per query block
+  constexpr int kWaves = BLK / 32;
+  constexpr int NT = 64 * kWaves;
+  constexpr int GPR = D * 2 / 16;
+  constexpr int NGS = QT * GPR;          // granules per Q (or dO) step tile
+  constexpr int NLD = NGS / NT;
+  constexpr int kLdGran = QT * 2 * 4 / 16;       // (lse, D) pairs of a step: 16 granules
+  constexpr int kLdLanes = kLdGran / kWaves;     // lanes per wave that move them
+  constexpr int kQk = D / 16, kPv = QT / 16, kOut = D / 32;
+  static_assert(NGS % NT == 0 && kLdGran % kWaves == 0, "tile shape");
+
+  __shared__ uint4 Qs[2][NGS];
+  __shared__ uint4 Gs[2][NGS];           // dO
+  __shared__ uint4 Ls[2][kLdGran];       // (lse * log2e, D) per query
+  __shared__ uint4 Vf[kQk][NT];          // each lane's V fragments (lane-private, k-major)
+
+  const int N = a.N, Nb = a.Nb, H = a.H;
+  const int total = a.B * H * Nb;
+  const int col = xcd_row(blockIdx.x, total);
+  const int bh = col / Nb, c = col - bh * Nb, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qn = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const int kk = c * BLK + w * 32 + qn;   // this lane's key (B-operand column, output row)
+  const T* Q = static_cast<const T*>(a.q);
+  const T* K = static_cast<const T*>(a.k);
+  const T* V = static_cast<const T*>(a.v);
+  const T* dO = static_cast<const T*>(a.dout);
+
+  const int f0 = __builtin_amdgcn_readfirstlane(a.col_ptr[col]);
+  int f1 = __builtin_amdgcn_readfirstlane(a.col_ptr[col + 1]);
+  if ((a.skip_bits[h >> 5] >> (h & 31)) & 1u) f1 = f0;
+
+  f32x16_t dk[kOut], dv[kOut];
+#pragma unroll
+  for (int io = 0; io < kOut; ++io) {
+    dk[io] = f32x16_t{};
+    dv[io] = f32x16_t{};
+  }
+
+  if (f1 > f0) {
+    // this lane's K fragments stay in registers; its V fragments are parked in LDS (only
+    // this lane reads them back), which keeps the accumulators out of scratch
+    Frag<T> kf[kQk];
+    const int kr = min(kk, N - 1);   // keys past N: any finite row (their outputs are not stored)
+#pragma unroll
+    for (int t = 0; t < kQk; ++t) {
+      kf[t] = lds_frag(K + head + (size_t)kr * D + 16 * t + 8 * hf);
+      Vf[t][tid] = lds_frag(V + head + (size_t)kr * D + 16 * t + 8 * hf).v;
+    }
+    const uint32_t wave_off = (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
+    const uint32_t q_lds[2] = {lds_addr(Qs[0]) + wave_off, lds_addr(Qs[1]) + wave_off};
+    const uint32_t g_lds[2] = {lds_addr(Gs[0]) + wave_off, lds_addr(Gs[1]) + wave_off};
+    const uint32_t l_off = (uint32_t)__builtin_amdgcn_readfirstlane(w) * (uint32_t)(kLdLanes * 16);
+    const uint32_t l_lds[2] = {lds_addr(Ls[0]) + l_off, lds_addr(Ls[1]) + l_off};
+    const int lg = w * kLdLanes + lane;   // (lse, D) granule moved by this lane (if < kLdGran)
+    auto dma_step = [&](int r, int hq, int slot, int nq) {
+      const size_t qrow0 = (size_t)r * BLK + hq * QT;
+      const T* qsrc = Q + head + qrow0 * D;
+      const T* gsrc = dO + head + qrow0 * D;
+      static_for<NLD>([&](auto it) {
+        const uint32_t o = dma_offset<T, D, NT>(it.value, tid, nq);
+        dma16<it.value * NT * 16>(qsrc, o, q_lds[slot]);
+        dma16<it.value * NT * 16>(gsrc, o, g_lds[slot]);
+      });
+      if (lane < kLdLanes) {
+        // granule lg holds queries 2lg, 2lg+1; past nq re-read the last valid pair
+        const int gq = min(lg, (nq - 1) >> 1);
+        dma16<0>(a.ld + 2 * ((size_t)bh * N + qrow0), (uint32_t)gq * 16u, l_lds[slot]);
+      }
+    };
+    // cursor over (query block r, step hq) of this key block's query blocks
+    int fbase = f0;
+    int rvec = f0 + lane < f1 ? a.row_idx[f0 + lane] : 0;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // K, V fragments and indices before transfers
+    int f = f0, hq = 0;
+    int r = __builtin_amdgcn_readlane(rvec, 0);
+    int nqb = min(BLK, N - r * BLK);
+    int slot = 0;
+    dma_step(r, 0, 0, min(QT, nqb));
+    for (;;) {
+      int f_n = f, hq_n = hq + 1, r_n = r, nqb_n = nqb;
+      if (hq_n >= kSteps || hq_n * QT >= nqb) {
+        f_n = f + 1;
+        hq_n = 0;
+        if (f_n < f1) {
+          if (f_n - fbase == 64) {
+            fbase += 64;
+            rvec = fbase + lane < f1 ? a.row_idx[fbase + lane] : 0;
+          }
+          r_n = __builtin_amdgcn_readlane(rvec, f_n - fbase);
+          nqb_n = min(BLK, N - r_n * BLK);
+        }
+      }
+      const bool more = f_n < f1;
+      const int nq = min(QT, nqb - hq * QT);
+
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wg_barrier();
+      if (more) dma_step(r_n, hq_n, slot ^ 1, min(QT, nqb_n - hq_n * QT));
+      const uint4* qt = Qs[slot];
+      const uint4* gt = Gs[slot];
+      const float* lt = reinterpret_cast<const float*>(Ls[slot]);
+
+      // S = Q K^T, dP = dO V^T (queries on rows, this lane's key on the column)
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int t = 0; t < kQk; ++t) {
+        Frag<T> qa, ga, va;
+        qa.v = qt[qn * GPR + ((2 * t + hf) ^ swz<GPR>(qn))];
+        ga.v = gt[qn * GPR + ((2 * t + hf) ^ swz<GPR>(qn))];
+        va.v = Vf[t][tid];
+        mma_k16(s, qa, kf[t]);
+        mma_k16(dp, ga, va);
+      }
+      // P = exp2(S scale log2e - lse log2e), dS = P (dP - D); queries past nq get 0
+      Frag<T> pf[kPv], dsf[kPv];
+#pragma unroll
+      for (int u = 0; u < kPv; ++u) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int j4 = 0; j4 < 2; ++j4) {
+          const int q0 = 16 * u + 8 * j4 + 4 * hf;   // 4 consecutive queries
+          const float4 l01 = *reinterpret_cast<const float4*>(lt + 2 * q0);
+          const float4 l23 = *reinterpret_cast<const float4*>(lt + 2 * q0 + 4);
+          const float ls[4] = {l01.x, l01.z, l23.x, l23.z};
+          const float ds_[4] = {l01.y, l01.w, l23.y, l23.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int i = 8 * u + 4 * j4 + t;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -ls[t]));
+            if (nq < QT && q0 + t >= nq) p = 0.f;
+            pv[4 * j4 + t] = p;
+            dsv[4 * j4 + t] = p * (dp[i] - ds_[t]);
+          }
+        }
+        pf[u] = pack_bf16(pv);
+        dsf[u] = pack_bf16(dsv);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transpose reads)
+      const uint16_t* qtile = reinterpret_cast<const uint16_t*>(qt);
+      const uint16_t* gtile = reinterpret_cast<const uint16_t*>(gt);
+#pragma unroll
+      for (int io = 0; io < kOut; ++io)
+#pragma unroll
+        for (int u = 0; u < kPv; ++u) {
+          mma_k16(dv[io], tr_frag<D>(gtile, io, u, lane), pf[u]);
+          mma_k16(dk[io], tr_frag<D>(qtile, io, u, lane), dsf[u]);
+        }
+
+      if (!more) break;
+      f = f_n;
+      hq = hq_n;
+      r = r_n;
+      nqb = nqb_n;
+      slot ^= 1;
+    }
+  }
+  if (kk < N) {
+    store_rows<kOut, D>(a.dk + head + (size_t)kk * D, dk, a.scale, hf);
+    store_rows<kOut, D>(a.dv + head + (size_t)kk * D, dv, 1.f, hf);
+  }
+}
+
+template <int D, int BLK>
+hipError_t launch_grads(const BwdArgs& a, hipStream_t s) {
+  const int rows = a.B * a.H * a.Nb;
+  hipLaunchKernelGGL((dq_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkv_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t bwd_workspace_layout(const BwdArgs& g, BwdArgs* a, void* base) {
+  const size_t rows = (size_t)g.B * g.H * g.Nb;
+  const size_t nq = (size_t)g.B * g.H * g.N;
+  size_t off = 0;
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  // (lse, D) pairs, padded so a step's 16-byte granules never pass the end
+  float* ld = static_cast<float*>(take((2 * nq + 64) * sizeof(float)));
+  int32_t* col_ptr = static_cast<int32_t*>(take((rows + 1) * sizeof(int32_t)));
+  int32_t* row_idx = static_cast<int32_t*>(take(rows * g.Nb * sizeof(int32_t)));
+  if (a) {
+    a->ld = ld;
+    a->col_ptr = col_ptr;
+    a->row_idx = row_idx;
+  }
+  return off;
+}
+
+hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t s) {
+  const size_t nq = (size_t)a.B * a.H * a.N;
+  const size_t threads = nq * (size_t)(a.d / 8);
+  const dim3 pgrid((unsigned)((threads + 255) / 256));
+  if (a.d == 128) {
+    if (a.o_bf16)
+      hipLaunchKernelGGL((bwd_prep_kernel<uint16_t, 128>), pgrid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.o), a.lse, a.ld, nq);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<float, 128>), pgrid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.dout), static_cast<const float*>(a.o), a.lse, a.ld, nq);
+  } else {
+    if (a.o_bf16)
+      hipLaunchKernelGGL((bwd_prep_kernel<uint16_t, 64>), pgrid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.o), a.lse, a.ld, nq);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<float, 64>), pgrid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.dout), static_cast<const float*>(a.o), a.lse, a.ld, nq);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csc_kernel, dim3((unsigned)(a.B * a.H)), dim3(kCscThreads), 0, s, a.row_ptr, a.col_idx,
+                     a.col_ptr, a.row_idx, a.Nb, a.B * a.H);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.d == 128 && a.blk == 128) return launch_grads<128, 128>(a, s);
+  if (a.d == 128 && a.blk == 64) return launch_grads<128, 64>(a, s);
+  if (a.d == 64 && a.blk == 128) return launch_grads<64, 128>(a, s);
+  return launch_grads<64, 64>(a, s);
+}
+
+}  // namespace asa

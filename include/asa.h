@@ -197,6 +197,57 @@ asa_status asa_attention_fwd(const void* Q, const void* K, const void* V, void* 
                              int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
                              const asa_head_pattern* patterns, float scale, void* stream);
 
+/*
+ * asa_attention_fwd_lse -- asa_attention_fwd that also returns what the backward needs to
+ * recompute the softmax weights: per query, the log of its normaliser.
+ *
+ * Source: Sparse-vDiT section 三 "核心公式" (the softmax of the masked attention).
+ * lse  device float32 [B,H,N]: lse_i = ln sum_{j in J_i} exp(scale * Q_i . K_j) over the
+ *      kept tokens J_i of query i's row; -INFINITY where the row is empty or the head is
+ *      ASA_PAT_SKIP.  Computed from the same running max and sum as O.
+ * All other arguments and errors as asa_attention_fwd; lse NULL is ASA_ERR_NULL_ARG.
+ */
+asa_status asa_attention_fwd_lse(const void* Q, const void* K, const void* V, void* O,
+                                 int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
+                                 const asa_head_pattern* patterns, float scale, float* lse,
+                                 void* stream);
+
+/* Workspace bytes for asa_attention_bwd: the per-query (lse, D) pairs and the transposed
+ * mask (key block -> query blocks), sized for the worst case B*H*Nb*Nb kept tiles.
+ * Returns 0 for an invalid shape (including Nb > 1024). */
+size_t asa_attention_bwd_workspace_size(const asa_shape* shape);
+
+/*
+ * asa_attention_bwd -- gradients of the block-sparse attention forward.
+ *
+ * Source: the masked attention of Sparse-vDiT section 三 "核心公式"; BLADE (abstract)
+ * trains the sparse attention jointly with step distillation, which needs its gradients.
+ * With P_ij = exp(scale Q_i.K_j - lse_i) over the kept tokens j of query i's CSR row:
+ *   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . V_j,   D_i = dO_i . O_i,
+ *   dS_ij = P_ij (dP_ij - D_i),   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i.
+ * dQ sums over each row's kept key blocks; dK and dV over the query blocks that keep each
+ * key block (the transposed mask, built in the workspace).  P and dS are rounded to bf16
+ * for the matrix products; all accumulation is fp32.  Deterministic (no atomics).
+ *
+ * Q, K, V, dO  device [B,H,N,d] bf16 (shape->in_dtype must be ASA_BF16; ASA_F32 inputs
+ *              return ASA_ERR_UNSUPPORTED).
+ * O            device [B,H,N,d] of o_dtype: the forward's output for the same inputs.
+ * lse          device float32 [B,H,N] from asa_attention_fwd_lse for the same inputs.
+ * dQ, dK, dV   device float32 [B,H,N,d], fully written (zero where no kept tile
+ *              contributes, and for ASA_PAT_SKIP heads).
+ * csr          the mask the forward used (col_idx entries in [0, Nb), unique per row).
+ * patterns     host array [H] or NULL; ASA_PAT_SKIP heads get zero gradients.
+ * scale        the forward's scale; <= 0 selects 1/sqrt(d).
+ * workspace    device buffer of at least asa_attention_bwd_workspace_size(shape) bytes,
+ *              256-byte aligned; its contents on entry are ignored.
+ * Limits: Nb <= 1024 (the transposed-mask builder), as for the mask builders.
+ */
+asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const void* O,
+                             int32_t o_dtype, const void* dO, const float* lse, float* dQ, float* dK,
+                             float* dV, const asa_shape* shape, const asa_csr* csr,
+                             const asa_head_pattern* patterns, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,7 +131,47 @@ def test_attention_rejects_arguments():
                 None) == BAD_PATTERN
 
 
+def test_attention_lse_rejects_arguments():
+    s = _shape()
+    csr = _csr(10)
+    call = asa.lib.asa_attention_fwd_lse
+    assert call(FAKE, FAKE, FAKE, FAKE, asa.ASA_F32, ctypes.byref(s), ctypes.byref(csr), None, 0.0, None,
+                None) == NULL_ARG                                   # lse NULL
+    assert "lse" in asa.lib.asa_last_error().decode()
+    assert call(FAKE, FAKE, FAKE, FAKE, 7, ctypes.byref(s), ctypes.byref(csr), None, 0.0, FAKE,
+                None) == BAD_DTYPE
+
+
+def _bwd(s, csr=None, ws=0x40000, ws_bytes=1 << 30, o_dtype=asa.ASA_F32, lse=FAKE, dq=FAKE, pats=None,
+         scale=0.0):
+    csr = csr or _csr(asa.lib.asa_csr_capacity(ctypes.byref(s)))
+    return asa.lib.asa_attention_bwd(FAKE, FAKE, FAKE, FAKE, o_dtype, FAKE, lse, dq, FAKE, FAKE,
+                                     ctypes.byref(s), ctypes.byref(csr), pats, scale, ctypes.c_void_p(ws),
+                                     ws_bytes, None)
+
+
+def test_attention_bwd_rejects_arguments():
+    s = _shape()
+    need = asa.lib.asa_attention_bwd_workspace_size(ctypes.byref(s))
+    assert need > 0
+    assert asa.lib.asa_attention_bwd_workspace_size(ctypes.byref(_shape(d=48))) == 0
+    assert asa.lib.asa_attention_bwd_workspace_size(ctypes.byref(_shape(N=64 * 1025, blk=64))) == 0   # Nb > 1024
+    assert _bwd(_shape(dt=asa.ASA_F32)) == UNSUPPORTED                 # bf16 inputs only
+    assert "ASA_BF16" in asa.lib.asa_last_error().decode()
+    assert _bwd(s, lse=None) == NULL_ARG
+    assert _bwd(s, dq=None) == NULL_ARG
+    assert _bwd(s, o_dtype=3) == BAD_DTYPE
+    assert _bwd(s, ws=0) == WORKSPACE
+    assert _bwd(s, ws_bytes=need - 1) == WORKSPACE
+    assert _bwd(s, ws=0x40010) == WORKSPACE                            # not 256-byte aligned
+    assert _bwd(s, scale=float("nan")) == BAD_PARAM
+    bad = (asa_head_pattern * 2)(asa_head_pattern(9, 0), asa_head_pattern(0, 0))
+    assert _bwd(s, pats=bad) == BAD_PATTERN
+    nullcsr = asa_csr(0, 0x30000, 10)
+    assert _bwd(s, csr=nullcsr) == NULL_ARG
+
+
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10000
+    assert asa.lib.asa_version() >= 10100

@@ -1,4 +1,5 @@
-"""Static checks on the generated gfx950 assembly of the attention kernels (CPU only).
+"""Static checks on the generated gfx950 assembly of the attention kernels, forward and
+backward (CPU only).
 
 The attention kernel issues its global -> LDS transfers from small inline-asm blocks.
 The compiler does not see inside them, so they must not touch state it relies on:
@@ -15,21 +16,21 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "block_sparse_attention_asa_amd", "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(ROOT, "block_sparse_attention_asa_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip")]
 HIPCC = "/opt/rocm/bin/hipcc"
 
 ALLOWED = {"s_mov_b32", "s_nop", "global_load_lds_dwordx4", "v_max3_f32"}
 
 
-@pytest.fixture(scope="module")
-def asm_text(tmp_path_factory):
+@pytest.fixture(scope="module", params=SRCS, ids=lambda p: os.path.basename(p))
+def asm_text(request, tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "attn_fwd.s"
+    out = tmp_path_factory.mktemp("asm") / (os.path.basename(request.param) + ".s")
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
            "-Xclang", "-packed-fp32-ops", f"-I{ROOT}/include",
            f"-I{ROOT}/block_sparse_attention_asa_amd/csrc", "-x", "hip", "-S", "--offload-device-only",
-           SRC, "-o", str(out)]
+           request.param, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
 
