@@ -46,11 +46,14 @@ def load_traffic(kernel_tag):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, rec.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if digest != rec.get("source_sha256"):
+    srcs = rec.get("sources") or [rec.get("source", "")]
+    h = hashlib.sha256()
+    for rel in srcs:                      # the kernel's source files, in the recorded order
+        src = os.path.join(ROOT, rel)
+        if not rel or not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != rec.get("source_sha256"):
         return None
     return rec.get("bytes_per_launch")
 
