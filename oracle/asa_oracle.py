@@ -27,6 +27,11 @@ What it computes, in the order the method applies it:
   row's softmax normaliser (what a training forward keeps for the backward).
   BLADE trains the sparse attention jointly with step distillation (abstract).
 
+* Per-head pattern search -- Sparse-vDiT, section 三: the offline search loss
+  L_i = MSE(O_i - O_0) + lambda (1 - S_i) over the candidate patterns, and the
+  selection formula (full attention when every L_i exceeds epsilon, else the
+  candidate with the smallest L_i), one layer of its offline search algorithm.
+
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against closed forms, library routines (torch SDPA and its autograd, scipy
 softmax / logsumexp), finite differences and brute force.  The pooled-score rule and the tuned top-k are specification choices:
@@ -261,7 +266,7 @@ def to_csr(M: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def density(M: np.ndarray, heads: Optional[Sequence[int]] = None) -> float:
-    """Fraction of kept tiles (1 - sparsity S_i in the Sparse-vDiT search loss)."""
+    """Fraction of kept tiles."""
     if heads is not None:
         M = M[:, list(heads)]
     return float(M.mean())
@@ -441,3 +446,79 @@ def attention_bwd_flops(M: np.ndarray, N: int, blk: int, d: int) -> float:
     """Algorithmic backward flops: sum over kept tiles of 10 * n_r * n_c * d (the five
     products s, dP, dv, dq, dk at 2 flops per multiply-add)."""
     return 2.5 * kept_tile_flops(M, N, blk, d)
+
+
+# ------------------------------------------------------------------------ pattern search
+# Sparse-vDiT ("Sparse-vDiT: Sparse Attention Acceleration for Video Diffusion
+# Transformers"), section 三: the offline search loss and the pattern-selection formula,
+# and the per-layer step of "Algorithm 1: Offline Sparse Diffusion Search".  For one layer
+# and one set of Q, K, V the search runs full attention (M0) and every candidate pattern,
+# scores each candidate by how far its output is from full attention plus a penalty for
+# the compute it keeps, and picks a pattern per head.
+# Readings where the page is terse:
+#   * MSE(O_i - O_0) of a head is the mean of the squared difference over the head's
+#     B x N x d output elements (the page's attention output is B x N x d per head).
+#   * S_i, the sparsity of pattern i, is the fraction of the N x N (query, key) token pairs
+#     it drops, with each kept tile counted at its true size (so M0 -> 0 and M1 -> 1, as
+#     the mode table lists).  When the pattern is the same for every batch element this
+#     is the same for all heads.
+#   * argmin ties go to the lowest candidate index; "L_i > epsilon" is strict.
+
+def pattern_sparsity(pattern: int, param: int, N: int, blk: int) -> float:
+    """S_i: fraction of the N*N token pairs that a static pattern does not attend."""
+    Nb = num_blocks(N, blk)
+    sizes = np.array([block_range(c, N, blk)[1] - block_range(c, N, blk)[0] for c in range(Nb)],
+                     dtype=np.int64)
+    kept = 0
+    for r in range(Nb):
+        row = static_row(pattern, param, r, N, blk)
+        kept += int(sizes[r]) * int(sizes[row].sum())
+    return 1.0 - kept / float(N * N)
+
+
+def pattern_mse(O_i: np.ndarray, O_0: np.ndarray) -> np.ndarray:
+    """MSE(O_i - O_0) per head: mean over (b, n, d) of the squared difference -> [H]."""
+    diff = O_i.astype(np.float64) - O_0.astype(np.float64)
+    return (diff * diff).mean(axis=(0, 2, 3))
+
+
+def pattern_loss(mse: np.ndarray, sparsity: np.ndarray, lam: float) -> np.ndarray:
+    """L_i = MSE(O_i - O_0) + lam * (1 - S_i); mse [H, n], sparsity [n] -> [H, n]."""
+    return mse + lam * (1.0 - np.asarray(sparsity, dtype=np.float64))[None, :]
+
+
+def select_patterns(L: np.ndarray, eps: float) -> np.ndarray:
+    """Pattern choice per head: 0 (full attention, M0) when every candidate's L_i exceeds
+    eps, else 1 + the index of the smallest L_i (first one on ties).  L is [H, n]."""
+    H, n = L.shape
+    choice = np.zeros(H, dtype=np.int64)
+    for h in range(H):
+        if n == 0 or np.all(L[h] > eps):
+            continue
+        choice[h] = 1 + int(np.argmin(L[h]))
+    return choice
+
+
+def pattern_search(Q: np.ndarray, K: np.ndarray, V: np.ndarray, blk: int,
+                   candidates: Sequence[Tuple[int, int]], lam: float, eps: float,
+                   O_0: Optional[np.ndarray] = None, outputs: Optional[Sequence[np.ndarray]] = None):
+    """One layer of the offline search.  candidates: static (pattern id, param) pairs, the
+    page's M1..M4.  Returns (choice [H], L [H, n], mse [H, n], S [n]).
+
+    O_0 / outputs, when given, are used instead of computing full attention / each
+    candidate's attention (to score outputs produced elsewhere with the same rule)."""
+    B, H, N, d = Q.shape
+    if O_0 is None:
+        O_0 = dense_attention(Q, K, V)
+    n = len(candidates)
+    mse = np.zeros((H, n), dtype=np.float64)
+    S = np.zeros(n, dtype=np.float64)
+    for i, (pid, prm) in enumerate(candidates):
+        S[i] = pattern_sparsity(pid, prm, N, blk)
+        if outputs is not None:
+            O_i = outputs[i]
+        else:
+            O_i = attention(Q, K, V, static_mask(B, H, N, blk, [(pid, prm)] * H), blk)
+        mse[:, i] = pattern_mse(O_i, O_0)
+    L = pattern_loss(mse, S, lam)
+    return select_patterns(L, eps), L, mse, S

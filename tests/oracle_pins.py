@@ -397,6 +397,120 @@ def check_lse_matches_scipy():
     assert np.all(np.isneginf(L[0, 1, 64:]))
 
 
+# ------------------------------------------------------------------ pattern search pins
+def check_pattern_sparsity_token_pairs():
+    """S_i = fraction of dropped token pairs, by enumerating the token-level mask (ragged
+    blocks count at their true size), plus the closed forms of the mode table."""
+    for N, blk in ((300, 32), (130, 16), (256, 64)):
+        Nb = O.num_blocks(N, blk)
+        blk_of = np.arange(N) // blk
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        for pid, prm in ((O.DIAG, 0), (O.VSTRIPE, 2), (O.MULTIDIAG, 5), (O.MULTIDIAG, 48),
+                         (O.FULL, 0), (O.SKIP, 0)):
+            if pid == O.MULTIDIAG:
+                hit = ((j - i) % prm) == 0            # token pairs on the diagonals
+                tile = np.zeros((Nb, Nb), dtype=bool)
+                np.logical_or.at(tile, (blk_of[:, None].repeat(N, 1), blk_of[None, :].repeat(N, 0)), hit)
+            elif pid == O.DIAG:
+                tile = np.eye(Nb, dtype=bool)
+            elif pid == O.VSTRIPE:
+                tile = np.zeros((Nb, Nb), dtype=bool)
+                tile[:, :prm] = True
+            else:
+                tile = np.full((Nb, Nb), pid == O.FULL)
+            tok = tile[blk_of][:, blk_of]
+            want = 1.0 - tok.sum() / float(N * N)
+            got = O.pattern_sparsity(pid, prm, N, blk)
+            assert abs(got - want) < 1e-15, (N, blk, pid, prm, got, want)
+    assert O.pattern_sparsity(O.FULL, 0, 300, 32) == 0.0
+    assert O.pattern_sparsity(O.SKIP, 0, 300, 32) == 1.0
+    assert abs(O.pattern_sparsity(O.DIAG, 0, 1024, 64) - (1 - 1 / 16)) < 1e-15
+    assert abs(O.pattern_sparsity(O.VSTRIPE, 3, 1000, 64) - (1 - 3 * 64 / 1000)) < 1e-15
+
+
+def _masked_sdpa_or_zero(q, k, v, tok):
+    """torch SDPA (float64, boolean token mask) per head; rows with no kept key -> 0."""
+    t = [torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v)]
+    m = torch.from_numpy(np.ascontiguousarray(tok))
+    out = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=m)
+    out = torch.where(m.any(dim=-1, keepdim=True), out, torch.zeros_like(out))
+    return out.numpy()
+
+
+def check_pattern_mse_matches_torch():
+    """MSE(O_i - O_0) per head: candidates' outputs from torch SDPA with the token mask,
+    the squared error from torch's mse_loss on each head's [B, N, d] slice."""
+    B, H, N, d, blk = 2, 3, 200, 16, 64
+    q, k, v = _qkv(B, H, N, d, 41)
+    v[:, 1] *= 3.0                                     # heads on different scales
+    cands = [(O.SKIP, 0), (O.DIAG, 0), (O.MULTIDIAG, 50), (O.VSTRIPE, 1)]
+    choice, L, mse, S = O.pattern_search(q, k, v, blk, cands, lam=0.01, eps=0.1)
+    o0 = _sdpa(q, k, v)
+    for n, (pid, prm) in enumerate(cands):
+        tok = _token_mask(O.static_mask(B, H, N, blk, [(pid, prm)] * H), N, blk)
+        oi = _masked_sdpa_or_zero(q, k, v, tok)
+        for h in range(H):
+            want = torch.nn.functional.mse_loss(torch.from_numpy(oi[:, h]), torch.from_numpy(o0[:, h])).item()
+            assert abs(mse[h, n] - want) <= 1e-13 * max(1.0, want), (n, h, mse[h, n], want)
+    assert L.shape == (H, len(cands)) and choice.shape == (H,)
+
+
+def check_pattern_uniform_attention_closed_form():
+    """Q = 0 makes every row's weights uniform over its kept tokens, so each output row is
+    the mean of V over those tokens: full -> mean over all N, diagonal -> mean over the
+    query's own block, stripe(s) -> mean over the first s blocks, skip -> 0.  The losses
+    and the choice follow from these means alone."""
+    B, H, N, d, blk = 1, 4, 320, 8, 64                 # 5 blocks
+    rng = RNG(43)
+    k = rng.standard_normal((B, H, N, d))
+    q = np.zeros((B, H, N, d))
+    offs = rng.standard_normal((B, H, 5, d))
+    v = np.repeat(offs, blk, axis=2) + 0.1 * rng.standard_normal((B, H, N, d))
+    v[:, 0] *= 0.05                                    # tiny outputs: skipping is cheapest
+    v[:, 1] *= 3.0                                     # large spread: every L_i > eps
+    v[:, 2] *= 0.2
+    v[:, 3] = np.repeat(offs[:, 3, :1], N, axis=1) * 0.5 + 0.3   # block-constant rows -> diag exact
+    lam, eps = 0.01, 0.1
+    cands = [(O.SKIP, 0), (O.DIAG, 0), (O.VSTRIPE, 1)]
+    choice, L, mse, S = O.pattern_search(q, k, v, blk, cands, lam, eps)
+    want = np.zeros((H, 3))
+    for h in range(H):
+        full = v[0, h].mean(axis=0)
+        blockmean = np.stack([v[0, h, r * blk:(r + 1) * blk].mean(axis=0) for r in range(5)])
+        diag_rows = np.repeat(blockmean, blk, axis=0)
+        stripe = v[0, h, :blk].mean(axis=0)
+        want[h, 0] = np.mean(full ** 2) + lam * 0.0
+        want[h, 1] = np.mean((diag_rows - full) ** 2) + lam * (5 * blk * blk) / N ** 2
+        want[h, 2] = np.mean((stripe - full) ** 2) + lam * (N * blk) / N ** 2
+    assert np.allclose(L, want, rtol=1e-12, atol=1e-15), (L, want)
+    assert np.allclose(S, [1.0, 1 - 1 / 5, 1 - 1 / 5], rtol=0, atol=1e-15)
+    # the branches this case was built to reach
+    assert choice[0] == 1 and choice[1] == 0 and choice[3] == 2, choice
+    assert np.array_equal(choice, O.select_patterns(want, eps))
+
+
+def check_select_rule_cases():
+    """The selection formula on hand-made losses: full attention only when every L_i is
+    strictly above eps; otherwise the smallest L_i, first index on ties."""
+    cases = [
+        ([[0.2, 0.3, 0.15]], 0.1, [0]),
+        ([[0.2, 0.05, 0.07]], 0.1, [2]),
+        ([[0.05, 0.05]], 0.1, [1]),
+        ([[0.1, 0.2]], 0.1, [1]),
+        ([[0.3, 0.09, 0.5]], 0.1, [2]),
+        ([[0.2, 0.3], [0.01, 0.02], [0.5, 0.11]], 0.1, [0, 1, 0]),
+        ([[0.12, 0.11]], 0.15, [2]),
+    ]
+    for L, eps, want in cases:
+        got = O.select_patterns(np.array(L), eps)
+        assert list(got) == want, (L, eps, got, want)
+    assert list(O.select_patterns(np.zeros((3, 0)), 0.1)) == [0, 0, 0]
+    # the loss adds lam * (1 - S_i): kept fraction 0.1 and 0.5 at lam 0.01
+    L = O.pattern_loss(np.array([[0.01, 0.02]]), np.array([0.9, 0.5]), 0.01)
+    assert np.allclose(L, [[0.011, 0.025]], rtol=0, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_dense_equals_sdpa, check_block_diagonal_equals_independent_blocks,
     check_weights_sum_to_one, check_identical_keys_give_mean_of_v,
@@ -408,4 +522,6 @@ ALL_CHECKS = [
     check_kept_tile_flops,
     check_bwd_finite_differences, check_bwd_matches_torch_autograd,
     check_bwd_identical_keys_closed_form, check_bwd_blocks_assemble_full, check_lse_matches_scipy,
+    check_pattern_sparsity_token_pairs, check_pattern_mse_matches_torch,
+    check_pattern_uniform_attention_closed_form, check_select_rule_cases,
 ]

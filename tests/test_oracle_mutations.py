@@ -118,6 +118,51 @@ def _lse_unscaled(Q, K, M, blk):
     return _orig_lse(Q * np.sqrt(d), K, M, blk)
 
 
+def _loss_no_penalty(mse, sparsity, lam):
+    return mse + 0.0 * lam
+
+
+def _loss_sparsity_not_density(mse, sparsity, lam):
+    return mse + lam * np.asarray(sparsity, dtype=np.float64)[None, :]
+
+
+def _select_variant(which):
+    def f(L, eps):
+        H, n = L.shape
+        out = np.zeros(H, dtype=np.int64)
+        for h in range(H):
+            if n == 0:
+                continue
+            if which == "ge" and np.all(L[h] >= eps):
+                continue
+            if which != "ge" and np.all(L[h] > eps):
+                continue
+            if which == "argmax":
+                out[h] = 1 + int(np.argmax(L[h]))
+            elif which == "last_tie":
+                out[h] = n - int(np.argmin(L[h][::-1]))
+            else:
+                out[h] = 1 + int(np.argmin(L[h]))
+        return out
+    return f
+
+
+def _mse_pooled_heads(O_i, O_0):
+    diff = O_i - O_0
+    return np.full(O_i.shape[1], (diff * diff).mean())
+
+
+def _mse_sum(O_i, O_0):
+    diff = O_i - O_0
+    return (diff * diff).sum(axis=(0, 2, 3))
+
+
+def _sparsity_tile_count(pattern, param, N, blk):
+    Nb = core.num_blocks(N, blk)
+    kept = sum(int(core.static_row(pattern, param, r, N, blk).sum()) for r in range(Nb))
+    return 1.0 - kept / float(Nb * Nb)
+
+
 MUTATIONS = {
     "pool_sum_not_mean": ("pool", _pool_sum),
     "pool_zero_padded_partial_block": ("pool", _pool_zero_padded),
@@ -134,6 +179,14 @@ MUTATIONS = {
     "bwd_dq_uses_v": ("_row_attention_bwd", _bwd_variant("dq_uses_v")),
     "bwd_dv_unnormalised": ("_row_attention_bwd", _bwd_variant("dv_unnormalised")),
     "lse_missing_scale": ("attention_lse", _lse_unscaled),
+    "search_loss_missing_penalty": ("pattern_loss", _loss_no_penalty),
+    "search_loss_sparsity_for_density": ("pattern_loss", _loss_sparsity_not_density),
+    "search_full_when_all_ge_eps": ("select_patterns", _select_variant("ge")),
+    "search_argmax": ("select_patterns", _select_variant("argmax")),
+    "search_last_index_on_ties": ("select_patterns", _select_variant("last_tie")),
+    "search_mse_pooled_over_heads": ("pattern_mse", _mse_pooled_heads),
+    "search_mse_sum_not_mean": ("pattern_mse", _mse_sum),
+    "search_sparsity_counts_tiles": ("pattern_sparsity", _sparsity_tile_count),
 }
 
 
