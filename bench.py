@@ -109,6 +109,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) timing")
+    ap.add_argument("--no-search", action="store_true", help="skip the per-head pattern search timing")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -226,6 +227,44 @@ def main():
         # five products per kept tile (S, dP, dV, dK, dQ): 2.5x the forward's flops
         result_extra["bwd_tflops"] = round(2.5 * flops / bwd_ms / 1e9, 2)
         del gout, grads, bws, lse
+
+    if not args.no_search:
+        # per-head pattern search over the page's four patterns: full attention (M0) plus
+        # each candidate through the same forward kernel, then the squared-error reductions
+        frame = cfg.Hs * cfg.Ws
+        cands = [(asa.SKIP, 0), (asa.DIAG, 0), (asa.MULTIDIAG, frame), (asa.VSTRIPE, 2)]
+        log(f"bench: pattern search, candidates {cands}")
+        sflops = 4.0 * d * float(N) * float(N) * H * B
+        for pid, prm in cands:
+            if pid == asa.SKIP:
+                continue
+            crp, cci = asa.asa_static_mask(B, H, N, blk, [(pid, prm)] * H, dev)
+            crp_h = crp.cpu().numpy()
+            sflops += kept_tile_flops(crp_h, cci[: int(crp_h[-1])].cpu().numpy(), N, blk, d, H, B)
+            del crp, cci
+        sws = torch.empty(int(asa.lib.asa_pattern_search_workspace_size(ctypes.byref(shp), len(cands))),
+                          dtype=torch.uint8, device=dev)
+        sres = (torch.empty(H, dtype=torch.int32, device=dev), torch.empty((H, len(cands)), dtype=torch.float64, device=dev),
+                torch.empty((H, len(cands)), dtype=torch.float64, device=dev))
+
+        def search():
+            asa.asa_pattern_search(xd["q"], xd["k"], xd["v"], blk, cands, lam=0.01, eps=0.1, workspace=sws, out=sres)
+
+        for _ in range(2):
+            search()
+        torch.cuda.synchronize()
+        ns = 5
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        sev[0].record(stream)
+        for _ in range(ns):
+            search()
+        sev[1].record(stream)
+        torch.cuda.synchronize()
+        search_ms = sev[0].elapsed_time(sev[1]) / ns
+        result_extra["search_ms"] = round(search_ms, 4)
+        result_extra["search_tflops"] = round(sflops / search_ms / 1e9, 2)
+        result_extra["search_choice"] = sres[0].cpu().tolist()
+        del sws, sres
 
     attn_tflops = flops / attn_ms / 1e9
     mask_bytes = 2.0 * B * H * N * d * 2 + 4.0 * (rows + 1 + kept)   # Q, K read once; CSR written

@@ -8,6 +8,8 @@ Entry points (same names as the C ABI in include/asa.h):
     asa_build_mask(q, k, blk, mode, ...)   -> (row_ptr, col_idx)
     asa_static_mask(B, H, N, blk, patterns, device) -> (row_ptr, col_idx)
     asa_attention_fwd(q, k, v, row_ptr, col_idx, blk, ...) -> O
+    asa_attention_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, blk, ...) -> (dQ, dK, dV)
+    asa_pattern_search(q, k, v, blk, candidates, ...) -> (choice, loss, mse)
 """
 import ctypes
 import os
@@ -69,6 +71,12 @@ EXPORTS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(asa_shape),
                                          ctypes.POINTER(asa_csr), ctypes.POINTER(asa_head_pattern),
                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "asa_pattern_search_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(asa_shape), ctypes.c_int32]),
+    "asa_pattern_search": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.POINTER(asa_shape), ctypes.POINTER(asa_head_pattern),
+                                          ctypes.c_int32, ctypes.c_double, ctypes.c_double, ctypes.c_float,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -321,6 +329,49 @@ def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     return dq, dk, dv
 
 
-__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attention_bwd", "asa_csr_capacity",
+def asa_pattern_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk: int,
+                       candidates: Sequence[Tuple[int, int]], *, lam: float = 0.01, eps: float = 0.1,
+                       scale: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                       out: Optional[Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]] = None,
+                       stream=None):
+    """Per-head pattern choice of one layer: returns (choice int32 [H], loss float64 [H, n],
+    mse float64 [H, n]) on the device.  choice 0 = full attention, i = candidates[i - 1]."""
+    _require_device(q, k, v)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must share one shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    shp = _shape_of(q, blk)
+    B, H, N, d = q.shape
+    n = len(candidates)
+    arr = (asa_head_pattern * max(n, 1))()
+    for i, (pid, prm) in enumerate(candidates):
+        arr[i].id, arr[i].param = int(pid), int(prm)
+    if out is None:
+        out = (torch.empty(H, dtype=torch.int32, device=q.device),
+               torch.empty((H, n), dtype=torch.float64, device=q.device),
+               torch.empty((H, n), dtype=torch.float64, device=q.device))
+    choice, loss, mse = out
+    _require_device(choice, loss, *( [mse] if mse is not None else []))
+    if choice.dtype != torch.int32 or choice.numel() != H:
+        raise ValueError("choice must be int32 [H]")
+    if loss.dtype != torch.float64 or loss.numel() != H * n:
+        raise ValueError("loss must be float64 [H, n]")
+    if mse is not None and (mse.dtype != torch.float64 or mse.numel() != H * n):
+        raise ValueError("mse must be float64 [H, n]")
+    need = int(lib.asa_pattern_search_workspace_size(ctypes.byref(shp), n))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.asa_pattern_search(q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(shp), arr, n,
+                                  float(lam), float(eps), float(scale),
+                                  loss.data_ptr(), mse.data_ptr() if mse is not None else None,
+                                  choice.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                  _stream(q.device, stream)),
+           "asa_pattern_search")
+    return choice, loss, mse
+
+
+__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attention_bwd", "asa_pattern_search",
+           "asa_csr_capacity",
            "AsaError", "lib", "LIB_PATH", "EXPORTS", "num_blocks",
            "ADAPTIVE", "FULL", "SKIP", "DIAG", "MULTIDIAG", "VSTRIPE", "TOPK", "TAU"]

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libasa.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["asa_api.cpp", "mask.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["asa_api.cpp", "mask.hip", "attn_fwd.hip", "attn_bwd.hip", "search.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -110,11 +110,65 @@ asa_status check_workspace(void* ws, size_t have, size_t need) {
   return ASA_OK;
 }
 
+// Workspace carve-up for asa_pattern_search (all offsets 256-byte aligned): the full
+// attention output O_0 and one candidate output (fp32 [B,H,N,d] each), one CSR mask with
+// the static builder's workspace, and the per-row partials of every candidate.
+struct SearchWorkspace {
+  float* o0;
+  float* oi;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  void* mask_ws;
+  double* sq;        // [n][B*H*Nb]
+  long long* pairs;  // [n][B*H*Nb]
+};
+
+size_t search_workspace_layout(const asa_shape* s, int n, SearchWorkspace* w, void* base) {
+  const asa::MaskGeom g = geom_of(s);
+  const size_t rows = (size_t)s->B * s->H * g.Nb;
+  const size_t out = (size_t)s->B * s->H * s->N * s->d * sizeof(float);
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    const size_t at = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return b ? b + at : nullptr;
+  };
+  SearchWorkspace t{};
+  t.o0 = reinterpret_cast<float*>(take(out));
+  t.oi = reinterpret_cast<float*>(take(out));
+  t.row_ptr = reinterpret_cast<int32_t*>(take((rows + 1) * sizeof(int32_t)));
+  t.col_idx = reinterpret_cast<int32_t*>(take(rows * (size_t)g.Nb * sizeof(int32_t)));
+  t.mask_ws = take(asa::mask_workspace_layout(g, false, nullptr, nullptr));
+  t.sq = reinterpret_cast<double*>(take((size_t)n * rows * sizeof(double)));
+  t.pairs = reinterpret_cast<long long*>(take((size_t)n * rows * sizeof(long long)));
+  if (w) *w = t;
+  return off;
+}
+
+asa::AttnArgs attn_args(const void* Q, const void* K, const void* V, void* O, bool out_bf16,
+                        const asa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                        const int32_t* order, float scale, float* lse) {
+  asa::AttnArgs a{};
+  a.q = Q; a.k = K; a.v = V; a.o = O;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.order = order;
+  a.lse = lse;
+  a.B = shape->B; a.H = shape->H; a.N = shape->N; a.d = shape->d; a.blk = shape->blk;
+  a.Nb = (int)num_blocks(shape);
+  a.in_bf16 = shape->in_dtype == ASA_BF16;
+  a.out_bf16 = out_bf16;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)shape->d);
+  a.scale_log2 = (float)(sc * 1.4426950408889634);   // log2(e)
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t asa_version(void) { return 10100; }
+int32_t asa_version(void) { return 10200; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {
@@ -232,18 +286,8 @@ static asa_status attention_fwd_impl(const void* Q, const void* K, const void* V
   asa::HeadTable heads;
   if ((st = fill_heads(shape, patterns, true, &heads)) != ASA_OK) return st;
 
-  asa::AttnArgs a{};
-  a.q = Q; a.k = K; a.v = V; a.o = O;
-  a.row_ptr = csr->row_ptr;
-  a.col_idx = csr->col_idx;
-  a.order = csr->order;
-  a.lse = lse;
-  a.B = shape->B; a.H = shape->H; a.N = shape->N; a.d = shape->d; a.blk = shape->blk;
-  a.Nb = (int)num_blocks(shape);
-  a.in_bf16 = shape->in_dtype == ASA_BF16;
-  a.out_bf16 = o_dtype == ASA_BF16;
-  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)shape->d);
-  a.scale_log2 = (float)(sc * 1.4426950408889634);   // log2(e)
+  asa::AttnArgs a = attn_args(Q, K, V, O, o_dtype == ASA_BF16, shape, csr->row_ptr, csr->col_idx,
+                              csr->order, scale, lse);
   if (patterns)
     for (int h = 0; h < shape->H; ++h)
       if (patterns[h].id == ASA_PAT_SKIP) a.skip_bits[h >> 5] |= 1u << (h & 31);
@@ -311,6 +355,84 @@ asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const 
       if (patterns[h].id == ASA_PAT_SKIP) a.skip_bits[h >> 5] |= 1u << (h & 31);
   hipError_t e = asa::launch_attention_bwd(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attention backward");
+  return ASA_OK;
+}
+
+size_t asa_pattern_search_workspace_size(const asa_shape* shape, int32_t n_candidates) {
+  if (check_shape(shape, true) != ASA_OK) return 0;
+  if (n_candidates < 0 || n_candidates > asa::kMaxSearchCandidates) return 0;
+  return search_workspace_layout(shape, n_candidates, nullptr, nullptr);
+}
+
+asa_status asa_pattern_search(const void* Q, const void* K, const void* V, const asa_shape* shape,
+                              const asa_head_pattern* candidates, int32_t n_candidates, double lambda,
+                              double eps, float scale, double* loss, double* mse, int32_t* choice,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  asa_status st = check_shape(shape, true);
+  if (st != ASA_OK) return st;
+  if (!Q || !K || !V) return fail(ASA_ERR_NULL_ARG, "Q, K or V is NULL");
+  if (!choice) return fail(ASA_ERR_NULL_ARG, "choice is NULL");
+  if (!loss && n_candidates > 0) return fail(ASA_ERR_NULL_ARG, "loss is NULL");
+  if (n_candidates < 0 || n_candidates > asa::kMaxSearchCandidates)
+    return fail(ASA_ERR_BAD_PARAM, "n_candidates=%d must lie in [0, %d]", n_candidates,
+                asa::kMaxSearchCandidates);
+  if (n_candidates > 0 && !candidates) return fail(ASA_ERR_NULL_ARG, "candidates is NULL");
+  for (int i = 0; i < n_candidates; ++i) {
+    const int id = candidates[i].id, prm = candidates[i].param;
+    if (id == ASA_PAT_ADAPTIVE || id < ASA_PAT_ADAPTIVE || id > ASA_PAT_VSTRIPE)
+      return fail(ASA_ERR_BAD_PATTERN, "candidate %d: pattern id %d is not a static pattern", i, id);
+    if (id == ASA_PAT_MULTIDIAG && prm <= 0)
+      return fail(ASA_ERR_BAD_PATTERN, "candidate %d: multi-diagonal stride %d must be > 0", i, prm);
+    if (id == ASA_PAT_VSTRIPE && prm < 0)
+      return fail(ASA_ERR_BAD_PATTERN, "candidate %d: vertical-stripe width %d must be >= 0", i, prm);
+  }
+  if (!std::isfinite(lambda) || !std::isfinite(eps))
+    return fail(ASA_ERR_BAD_PARAM, "lambda and eps must be finite");
+  if (!std::isfinite(scale)) return fail(ASA_ERR_BAD_PARAM, "scale must be finite");
+  const size_t need = search_workspace_layout(shape, n_candidates, nullptr, nullptr);
+  if ((st = check_workspace(workspace, workspace_bytes, need)) != ASA_OK) return st;
+
+  SearchWorkspace w;
+  search_workspace_layout(shape, n_candidates, &w, workspace);
+  const asa::MaskGeom g = geom_of(shape);
+  asa::MaskWorkspace mws;
+  asa::mask_workspace_layout(g, false, &mws, w.mask_ws);
+  const size_t rows = (size_t)shape->B * shape->H * g.Nb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  asa::HeadTable heads;
+
+  // M0: full attention, the reference every candidate is scored against.
+  std::memset(&heads, 0, sizeof(heads));
+  for (int h = 0; h < shape->H; ++h) heads.id[h] = ASA_PAT_FULL;
+  if ((e = asa::launch_static_rows(g, heads, mws, s)) != hipSuccess) return hip_fail(e, "full mask rows");
+  if ((e = asa::launch_csr(g, mws, w.row_ptr, w.col_idx, nullptr, s)) != hipSuccess) return hip_fail(e, "full mask csr");
+  asa::AttnArgs a = attn_args(Q, K, V, w.o0, false, shape, w.row_ptr, w.col_idx, nullptr, scale, nullptr);
+  if ((e = asa::launch_attention(a, s)) != hipSuccess) return hip_fail(e, "full attention");
+
+  for (int i = 0; i < n_candidates; ++i) {
+    const int id = candidates[i].id;
+    int prm = candidates[i].param;
+    if (id == ASA_PAT_VSTRIPE && prm > g.Nb) prm = g.Nb;
+    for (int h = 0; h < shape->H; ++h) { heads.id[h] = id; heads.param[h] = prm; }
+    if ((e = asa::launch_static_rows(g, heads, mws, s)) != hipSuccess) return hip_fail(e, "candidate mask rows");
+    if ((e = asa::launch_csr(g, mws, w.row_ptr, w.col_idx, nullptr, s)) != hipSuccess)
+      return hip_fail(e, "candidate mask csr");
+    const float* oi = nullptr;   // a skipped head's output is zero: nothing to compute
+    if (id != ASA_PAT_SKIP) {
+      a = attn_args(Q, K, V, w.oi, false, shape, w.row_ptr, w.col_idx, nullptr, scale, nullptr);
+      if ((e = asa::launch_attention(a, s)) != hipSuccess) return hip_fail(e, "candidate attention");
+      oi = w.oi;
+    }
+    if ((e = asa::launch_search_sq_err(w.o0, oi, w.row_ptr, w.col_idx, shape->B, shape->H, shape->N,
+                                       shape->d, shape->blk, g.Nb, w.sq + i * rows, w.pairs + i * rows, s)) !=
+        hipSuccess)
+      return hip_fail(e, "squared error");
+  }
+  if ((e = asa::launch_search_choose(w.sq, w.pairs, shape->B, shape->H, shape->N, shape->d, g.Nb, n_candidates,
+                                     lambda, eps, loss, mse, choice, s)) != hipSuccess)
+    return hip_fail(e, "choose");
   return ASA_OK;
 }
 

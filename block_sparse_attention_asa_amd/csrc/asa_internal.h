@@ -103,4 +103,15 @@ struct BwdArgs {
 size_t bwd_workspace_layout(const BwdArgs& geom, BwdArgs* a, void* base);
 hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t s);
 
+// Pattern search reductions.  sq_err: per CSR row, the float64 sum of (oi - o0)^2 over the
+// row's outputs (oi NULL = zero output) and its kept token pairs.  choose: per head, the
+// loss of each of n_cand candidates (partials laid out [n_cand][B*H*Nb]) and the choice.
+constexpr int kMaxSearchCandidates = 8;
+hipError_t launch_search_sq_err(const float* o0, const float* oi, const int32_t* row_ptr,
+                                const int32_t* col_idx, int B, int H, int N, int d, int blk, int Nb,
+                                double* sq, long long* pairs, hipStream_t s);
+hipError_t launch_search_choose(const double* sq, const long long* pairs, int B, int H, int N, int d,
+                                int Nb, int n_cand, double lam, double eps, double* loss, double* mse,
+                                int32_t* choice, hipStream_t s);
+
 }  // namespace asa

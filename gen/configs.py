@@ -44,6 +44,10 @@ class Config:
     keep_diag: int = 1
     patterns: Optional[List[Tuple[int, int]]] = None   # per head (id, param)
     target_density: Optional[float] = None              # for tuned top-k
+    # per-head multipliers of the generated Q and V (None = 1 for every head); they spread
+    # the heads over the regimes the pattern search tells apart
+    q_head_scale: Optional[List[float]] = None
+    v_head_scale: Optional[List[float]] = None
     notes: str = ""
 
     @property

@@ -17,9 +17,11 @@ Recipe (seed = config number, NumPy PCG64 via ``default_rng``):
      by a Gaussian of sigma 3 tokens over the two spatial axes (reflect borders,
      truncated at 4 sigma), rescaled per channel to unit standard deviation over
      the frame, then multiplied by 2.
-3. Tokens are laid out as text first, then frames in raster order (row-major
+3. Optional per-head multipliers (``q_head_scale``, ``v_head_scale``) scale head h of
+   Q and of V after step 2, in float32.
+4. Tokens are laid out as text first, then frames in raster order (row-major
    over ``Hs x Ws``).
-4. bf16 configs round the float32 values to bf16 with round-to-nearest-even
+5. bf16 configs round the float32 values to bf16 with round-to-nearest-even
    (``torch.Tensor.to(torch.bfloat16)``).
 """
 from dataclasses import replace
@@ -88,6 +90,10 @@ def make_inputs(cfg: Config) -> Dict[str, torch.Tensor]:
         k[:, :, t0:] += comp
         v[:, :, t0:] += comp
         del comp
+    if cfg.q_head_scale is not None:
+        q *= np.asarray(cfg.q_head_scale, dtype=np.float32)[None, :, None, None]
+    if cfg.v_head_scale is not None:
+        v *= np.asarray(cfg.v_head_scale, dtype=np.float32)[None, :, None, None]
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     return {name: torch.from_numpy(a).to(tdt).contiguous()
             for name, a in (("q", q), ("k", k), ("v", v))}

@@ -114,7 +114,8 @@ typedef struct asa_csr {
   int32_t* order;
 } asa_csr;
 
-/* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order. */
+/* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order;
+ * 1.2.0 added asa_pattern_search. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -247,6 +248,50 @@ asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const 
                              float* dV, const asa_shape* shape, const asa_csr* csr,
                              const asa_head_pattern* patterns, float scale, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for asa_pattern_search with n_candidates candidates: two fp32 [B,H,N,d]
+ * outputs (full attention and one candidate at a time), one CSR mask with the static
+ * builder's workspace, and per-row partial sums.  Returns 0 for an invalid shape
+ * (including Nb > 1024) or n_candidates outside [0, 8]. */
+size_t asa_pattern_search_workspace_size(const asa_shape* shape, int32_t n_candidates);
+
+/*
+ * asa_pattern_search -- one layer of the per-head sparse-pattern search.
+ *
+ * Source: Sparse-vDiT section 三, the offline search loss L_i = MSE(O_i - O_0) +
+ * lambda (1 - S_i), the pattern-selection formula, and the per-layer step of its offline
+ * sparse diffusion search (run M0 and each candidate, score, choose).  The page suggests
+ * lambda = 0.01, eps = 0.1 (its Table 3 ablation).  For every head h:
+ *   O_0      = full attention (M0) of the head, computed here with the forward kernel;
+ *   O_i      = the head's attention under candidate i's static pattern (zero for
+ *              ASA_PAT_SKIP), i = 1..n_candidates;
+ *   MSE_i[h] = mean over the head's B x N x d outputs of (O_i - O_0)^2, summed in float64
+ *              from the fp32 outputs;
+ *   S_i      = fraction of the N x N (query, key) token pairs the pattern does not attend
+ *              (a kept tile counts n_r * n_c pairs, so partial blocks count at their size);
+ *   L_i[h]   = MSE_i[h] + lambda * (1 - S_i);
+ *   choice[h] = 0 (full attention) if L_i[h] > eps for every i (strictly), else the 1-based
+ *              index of the smallest L_i[h] (the lowest index on ties).  n_candidates = 0
+ *              gives choice 0 everywhere.
+ * The reductions run in a fixed order: the results are deterministic.
+ *
+ * Q, K, V       device [B,H,N,d] of shape->in_dtype (attention as asa_attention_fwd, fp32 out).
+ * candidates    host array [n_candidates] of static patterns (any id but ASA_PAT_ADAPTIVE,
+ *               with that id's parameter rules), applied to every head; n_candidates <= 8.
+ * lambda, eps   finite; scale as asa_attention_fwd (<= 0 selects 1/sqrt(d)).
+ * loss          device float64 [H, n_candidates]: L_i[h] at h * n_candidates + (i - 1)
+ *               (may be NULL only when n_candidates is 0).
+ * mse           device float64 [H, n_candidates] or NULL: MSE_i[h], same layout.
+ * choice        device int32 [H].
+ * workspace     device buffer of at least asa_pattern_search_workspace_size() bytes,
+ *               256-byte aligned; its contents on entry are ignored.
+ * Errors: ASA_ERR_BAD_PATTERN for an adaptive/unknown candidate or a bad parameter,
+ * ASA_ERR_BAD_PARAM for n_candidates out of range or a non-finite lambda / eps / scale.
+ */
+asa_status asa_pattern_search(const void* Q, const void* K, const void* V, const asa_shape* shape,
+                              const asa_head_pattern* candidates, int32_t n_candidates, double lambda,
+                              double eps, float scale, double* loss, double* mse, int32_t* choice,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -171,7 +171,45 @@ def test_attention_bwd_rejects_arguments():
     assert _bwd(s, csr=nullcsr) == NULL_ARG
 
 
+def _search(s, cands=None, n=None, lam=0.01, eps=0.1, scale=0.0, loss=FAKE, choice=FAKE, ws=0x40000,
+            ws_bytes=1 << 30, q=FAKE):
+    if cands is None:
+        cands = [(asa.SKIP, 0), (asa.DIAG, 0)]
+    arr = (asa_head_pattern * max(len(cands), 1))(*[asa_head_pattern(i, p) for i, p in cands])
+    n = len(cands) if n is None else n
+    return asa.lib.asa_pattern_search(q, FAKE, FAKE, ctypes.byref(s), arr, n, lam, eps, scale, loss, None,
+                                      choice, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_pattern_search_rejects_arguments():
+    s = _shape()
+    need = asa.lib.asa_pattern_search_workspace_size(ctypes.byref(s), 2)
+    B, H, N, d, Nb = 1, 2, 1024, 64, 16
+    # two fp32 outputs dominate the workspace
+    assert need >= 2 * B * H * N * d * 4 + B * H * Nb * Nb * 4
+    assert asa.lib.asa_pattern_search_workspace_size(ctypes.byref(s), 9) == 0
+    assert asa.lib.asa_pattern_search_workspace_size(ctypes.byref(s), -1) == 0
+    assert asa.lib.asa_pattern_search_workspace_size(ctypes.byref(_shape(N=64 * 1025, blk=64)), 2) == 0
+    assert _search(s, q=None) == NULL_ARG
+    assert _search(s, loss=None) == NULL_ARG
+    assert _search(s, choice=None) == NULL_ARG
+    assert _search(s, n=9) == BAD_PARAM
+    assert _search(s, n=-1) == BAD_PARAM
+    assert _search(s, cands=[(asa.ADAPTIVE, 0)]) == BAD_PATTERN
+    assert "candidate 0" in asa.lib.asa_last_error().decode()
+    assert _search(s, cands=[(asa.SKIP, 0), (asa.MULTIDIAG, 0)]) == BAD_PATTERN
+    assert _search(s, cands=[(asa.VSTRIPE, -1)]) == BAD_PATTERN
+    assert _search(s, cands=[(11, 0)]) == BAD_PATTERN
+    assert _search(s, lam=float("inf")) == BAD_PARAM
+    assert _search(s, eps=float("nan")) == BAD_PARAM
+    assert _search(s, scale=float("nan")) == BAD_PARAM
+    assert _search(s, ws=0) == WORKSPACE
+    assert _search(s, ws_bytes=need - 1) == WORKSPACE
+    assert _search(s, ws=0x40010) == WORKSPACE
+    assert _search(_shape(d=96)) == UNSUPPORTED
+
+
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10100
+    assert asa.lib.asa_version() >= 10200
