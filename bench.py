@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) timing")
     ap.add_argument("--no-search", action="store_true", help="skip the per-head pattern search timing")
+    ap.add_argument("--no-split", action="store_true", help="skip the split-row timing (one head in full)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,6 +266,42 @@ def main():
         result_extra["search_tflops"] = round(sflops / search_ms / 1e9, 2)
         result_extra["search_choice"] = sres[0].cpu().tolist()
         del sws, sres
+
+    if not args.no_split:
+        # few rows: one head of the layer attended in full (256 rows of 256 blocks) fills
+        # only part of the chip; the split forward cuts each row into chunks
+        log("bench: one head in full, plain and split forward")
+        h1 = {k: t[:, :1].contiguous() for k, t in xd.items()}
+        frp, fci = asa.asa_static_mask(B, 1, N, blk, [(asa.FULL, 0)], dev)
+        fo = torch.empty((B, 1, N, d), dtype=torch.float32, device=dev)
+        shp1 = asa.asa_shape(B, 1, N, d, blk, asa.ASA_BF16)
+        fws = torch.empty(max(1, int(asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(shp1), 0))),
+                          dtype=torch.uint8, device=dev)
+
+        def one_head(split):
+            if split:
+                asa.asa_attention_fwd_split(h1["q"], h1["k"], h1["v"], frp, fci, blk, split_blocks=0, out=fo,
+                                            workspace=fws)
+            else:
+                asa.asa_attention_fwd(h1["q"], h1["k"], h1["v"], frp, fci, blk, out=fo)
+
+        hflops = 4.0 * d * float(N) * float(N) * B
+        for split in (False, True):
+            for _ in range(3):
+                one_head(split)
+            torch.cuda.synchronize()
+            hev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            hev[0].record(stream)
+            for _ in range(10):
+                one_head(split)
+            hev[1].record(stream)
+            torch.cuda.synchronize()
+            hms = hev[0].elapsed_time(hev[1]) / 10
+            key = "split" if split else "nosplit"
+            result_extra[f"{key}_ms"] = round(hms, 4)
+            result_extra[f"{key}_tflops"] = round(hflops / hms / 1e9, 2)
+        result_extra["split_case"] = f"one head in full: B={B} H=1 N={N} d={d} blk={blk}, automatic split"
+        del h1, frp, fci, fo, fws
 
     attn_tflops = flops / attn_ms / 1e9
     mask_bytes = 2.0 * B * H * N * d * 2 + 4.0 * (rows + 1 + kept)   # Q, K read once; CSR written

@@ -8,6 +8,7 @@ Entry points (same names as the C ABI in include/asa.h):
     asa_build_mask(q, k, blk, mode, ...)   -> (row_ptr, col_idx)
     asa_static_mask(B, H, N, blk, patterns, device) -> (row_ptr, col_idx)
     asa_attention_fwd(q, k, v, row_ptr, col_idx, blk, ...) -> O
+    asa_attention_fwd_split(q, k, v, row_ptr, col_idx, blk, split_blocks=...) -> O
     asa_attention_bwd(q, k, v, o, dout, lse, row_ptr, col_idx, blk, ...) -> (dQ, dK, dV)
     asa_pattern_search(q, k, v, blk, candidates, ...) -> (choice, loss, mse)
 """
@@ -65,6 +66,11 @@ EXPORTS = {
                                              ctypes.c_int32, ctypes.POINTER(asa_shape), ctypes.POINTER(asa_csr),
                                              ctypes.POINTER(asa_head_pattern), ctypes.c_float, ctypes.c_void_p,
                                              ctypes.c_void_p]),
+    "asa_attention_fwd_split_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(asa_shape), ctypes.c_int32]),
+    "asa_attention_fwd_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.POINTER(asa_shape), ctypes.POINTER(asa_csr),
+                                               ctypes.POINTER(asa_head_pattern), ctypes.c_float, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "asa_attention_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(asa_shape)]),
     "asa_attention_bwd": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -288,6 +294,48 @@ def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr
     return out
 
 
+def asa_attention_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr: torch.Tensor,
+                            col_idx: torch.Tensor, blk: int, *, split_blocks: int = 0,
+                            patterns: Optional[Sequence[Tuple[int, int]]] = None,
+                            out_dtype: torch.dtype = torch.float32, scale: float = 0.0,
+                            order: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """asa_attention_fwd with rows of more than `split_blocks` kept blocks split over several
+    workgroups and merged afterwards (0 = choose from the shape).  Returns O [B,H,N,d]."""
+    _require_device(q, k, v, row_ptr, col_idx)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise TypeError("row_ptr and col_idx must be int32")
+    shp = _shape_of(q, blk)
+    B, H, N, d = q.shape
+    if row_ptr.numel() != B * H * num_blocks(N, blk) + 1:
+        raise ValueError("row_ptr length does not match [B, H, Nb] rows")
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    _require_device(out)
+    if order is not None:
+        _require_device(order)
+        if order.dtype != torch.int32 or order.numel() != row_ptr.numel() - 1:
+            raise ValueError("order must be int32 with one entry per CSR row")
+    if lse is not None:
+        _require_device(lse)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be float32 [B, H, N]")
+    need = int(lib.asa_attention_fwd_split_workspace_size(ctypes.byref(shp), int(split_blocks)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    csr = _csr_struct(row_ptr, col_idx, order)
+    _check(lib.asa_attention_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dtype_code(out),
+                                       ctypes.byref(shp), ctypes.byref(csr), _patterns(patterns, H), float(scale),
+                                       lse.data_ptr() if lse is not None else None, int(split_blocks),
+                                       workspace.data_ptr() if workspace is not None else None,
+                                       workspace.numel() if workspace is not None else 0,
+                                       _stream(q.device, stream)), "asa_attention_fwd_split")
+    return out
+
+
 def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                       dout: torch.Tensor, lse: torch.Tensor, row_ptr: torch.Tensor,
                       col_idx: torch.Tensor, blk: int, *,
@@ -371,7 +419,8 @@ def asa_pattern_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk: i
     return choice, loss, mse
 
 
-__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attention_bwd", "asa_pattern_search",
+__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attention_fwd_split",
+           "asa_attention_bwd", "asa_pattern_search",
            "asa_csr_capacity",
            "AsaError", "lib", "LIB_PATH", "EXPORTS", "num_blocks",
            "ADAPTIVE", "FULL", "SKIP", "DIAG", "MULTIDIAG", "VSTRIPE", "TOPK", "TAU"]

@@ -164,11 +164,51 @@ asa::AttnArgs attn_args(const void* Q, const void* K, const void* V, void* O, bo
   return a;
 }
 
+// Split-row plan: chunk length T (kept blocks per workgroup) and chunks per row at most.
+// split_blocks = 0 chooses T from the shape: a launch of fewer than kSplitRows rows (about
+// 1.5 workgroups per compute unit) leaves compute units idle, so each row is cut into
+// ceil(kSplitRows / rows) chunks, none shorter than kMinChunk blocks (shorter chunks cost
+// more in partial outputs than they gain).  A plan that can never split a row returns 0.
+constexpr int64_t kSplitRows = 384;
+constexpr int64_t kMinChunk = 16;
+
+int split_plan(const asa_shape* s, int32_t split_blocks, int* split_max) {
+  const int64_t Nb = num_blocks(s);
+  const int64_t rows = (int64_t)s->B * s->H * Nb;
+  int64_t t = split_blocks;
+  if (t == 0) {
+    if (rows >= kSplitRows) {
+      *split_max = 1;
+      return 0;
+    }
+    const int64_t n = (kSplitRows + rows - 1) / rows;
+    t = (Nb + n - 1) / n;
+    if (t < kMinChunk) t = kMinChunk;
+    const int64_t floor_t = (Nb + asa::kMaxSplit - 1) / asa::kMaxSplit;
+    if (t < floor_t) t = floor_t;
+  }
+  if (t >= Nb) {
+    *split_max = 1;
+    return 0;
+  }
+  *split_max = (int)((Nb + t - 1) / t);
+  return (int)t;
+}
+
+size_t split_workspace_layout(const asa_shape* s, int split_max, float** part_o, float** part_ml, void* base) {
+  const size_t rows = (size_t)s->B * s->H * num_blocks(s);
+  const size_t o_bytes = ((size_t)split_max * rows * s->blk * s->d * sizeof(float) + 255) & ~(size_t)255;
+  const size_t ml_bytes = ((size_t)split_max * rows * s->blk * 2 * sizeof(float) + 255) & ~(size_t)255;
+  if (part_o) *part_o = base ? reinterpret_cast<float*>(base) : nullptr;
+  if (part_ml) *part_ml = base ? reinterpret_cast<float*>(static_cast<char*>(base) + o_bytes) : nullptr;
+  return o_bytes + ml_bytes;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t asa_version(void) { return 10200; }
+int32_t asa_version(void) { return 10300; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {
@@ -272,7 +312,9 @@ asa_status asa_static_mask(const asa_shape* shape, const asa_head_pattern* patte
 static asa_status attention_fwd_impl(const void* Q, const void* K, const void* V, void* O,
                                      int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
                                      const asa_head_pattern* patterns, float scale, float* lse,
-                                     bool need_lse, void* stream) {
+                                     bool need_lse, void* stream, bool split_call = false,
+                                     int32_t split_blocks = 0, void* workspace = nullptr,
+                                     size_t workspace_bytes = 0) {
   g_last_error[0] = '\0';
   if (need_lse && !lse) return fail(ASA_ERR_NULL_ARG, "lse is NULL");
   asa_status st = check_shape(shape, false);
@@ -291,8 +333,25 @@ static asa_status attention_fwd_impl(const void* Q, const void* K, const void* V
   if (patterns)
     for (int h = 0; h < shape->H; ++h)
       if (patterns[h].id == ASA_PAT_SKIP) a.skip_bits[h >> 5] |= 1u << (h & 31);
-  hipError_t e = asa::launch_attention(a, static_cast<hipStream_t>(stream));
+  if (split_call) {
+    if (split_blocks < 0) return fail(ASA_ERR_BAD_PARAM, "split_blocks=%d must be >= 0", split_blocks);
+    int smax = 1;
+    const int t = split_plan(shape, split_blocks, &smax);
+    if (smax > asa::kMaxSplit)
+      return fail(ASA_ERR_BAD_PARAM, "split_blocks=%d cuts a %lld-block row into more than %d chunks", split_blocks,
+                  (long long)num_blocks(shape), asa::kMaxSplit);
+    if (t > 0) {
+      const size_t need = split_workspace_layout(shape, smax, nullptr, nullptr, nullptr);
+      if ((st = check_workspace(workspace, workspace_bytes, need)) != ASA_OK) return st;
+      a.split_blocks = t;
+      a.split_max = smax;
+      split_workspace_layout(shape, smax, &a.part_o, &a.part_ml, workspace);
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = asa::launch_attention(a, s);
   if (e != hipSuccess) return hip_fail(e, "attention");
+  if (a.split_blocks > 0 && (e = asa::launch_split_combine(a, s)) != hipSuccess) return hip_fail(e, "split combine");
   return ASA_OK;
 }
 
@@ -307,6 +366,22 @@ asa_status asa_attention_fwd_lse(const void* Q, const void* K, const void* V, vo
                                  const asa_head_pattern* patterns, float scale, float* lse,
                                  void* stream) {
   return attention_fwd_impl(Q, K, V, O, o_dtype, shape, csr, patterns, scale, lse, true, stream);
+}
+
+size_t asa_attention_fwd_split_workspace_size(const asa_shape* shape, int32_t split_blocks) {
+  if (check_shape(shape, false) != ASA_OK || split_blocks < 0) return 0;
+  int smax = 1;
+  if (split_plan(shape, split_blocks, &smax) == 0 || smax > asa::kMaxSplit) return 0;
+  return split_workspace_layout(shape, smax, nullptr, nullptr, nullptr);
+}
+
+asa_status asa_attention_fwd_split(const void* Q, const void* K, const void* V, void* O, int32_t o_dtype,
+                                   const asa_shape* shape, const asa_csr* csr,
+                                   const asa_head_pattern* patterns, float scale, float* lse,
+                                   int32_t split_blocks, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return attention_fwd_impl(Q, K, V, O, o_dtype, shape, csr, patterns, scale, lse, false, stream, true,
+                            split_blocks, workspace, workspace_bytes);
 }
 
 size_t asa_attention_bwd_workspace_size(const asa_shape* shape) {

@@ -72,9 +72,19 @@ struct AttnArgs {
   bool in_bf16, out_bf16;
   float scale_log2;      // softmax scale times log2(e)
   uint32_t skip_bits[kMaxHeads / 32];   // heads whose output is zero
+  // Split rows (0 = off): a row keeping more than split_blocks key blocks is cut into
+  // ceil(count / split_blocks) chunks of near-equal length, one workgroup each.  Chunks
+  // write unnormalised partials; launch_split_combine merges them into O (and lse).
+  int32_t split_blocks;
+  int32_t split_max;     // chunks per row at most: ceil(Nb / split_blocks)
+  float* part_o;         // [split_max][B*H*Nb][blk][d] fp32 partial O (unnormalised)
+  float* part_ml;        // [split_max][B*H*Nb][blk][2] running max (log2 units) and sum
 };
 
+constexpr int kMaxSplit = 64;   // chunks per row at most
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+hipError_t launch_split_combine(const AttnArgs& a, hipStream_t s);
 
 // Attention backward (bf16 inputs, fp32 gradients).
 struct BwdArgs {

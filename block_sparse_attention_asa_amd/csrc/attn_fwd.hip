@@ -30,7 +30,9 @@ namespace {
 // Each kept key block is consumed in steps of KT keys.  K and V of a step share one slot of
 // a two-slot LDS ring: while the workgroup computes on one slot, the next step's K and V
 // stream into the other, so a step needs a single barrier.
-template <typename T, typename TO, int D, int BLK>
+// kSplit: the launch cuts long rows into chunks (meta.split_blocks > 0); a separate
+// instantiation keeps the registers of the plain kernel untouched.
+template <typename T, typename TO, int D, int BLK, bool kSplit>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, TO* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int N, int Nb,
@@ -58,9 +60,23 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   __shared__ uint4 Kt[2][NGS];
   __shared__ uint4 Vt[2][NGS];
 
-  // position in the processing order -> row (a permutation from the mask builder, which
-  // lists long rows first inside each XCD's range, or the identity)
-  const int pos = xcd_row(blockIdx.x, total_rows);
+  // work item -> position in the processing order (and, with split rows, the chunk of the
+  // row).  Positions map to rows through a permutation from the mask builder, which lists
+  // long rows first inside each XCD's range, or the identity.
+  int pos, chunk = 0;
+  if constexpr (kSplit) {
+    // each XCD walks its own range of rows, all chunks of a row together; the grid is
+    // padded to 8 equal shares, so surplus items exit
+    const int x = blockIdx.x % kXcds, t = blockIdx.x / kXcds;
+    int lo, hi;
+    xcd_range(x, total_rows, lo, hi);
+    const int pl = t / meta.split_max;
+    if (pl >= hi - lo) return;
+    chunk = t - pl * meta.split_max;
+    pos = lo + pl;
+  } else {
+    pos = xcd_row(blockIdx.x, total_rows);
+  }
   const int row = meta.order ? __builtin_amdgcn_readfirstlane(meta.order[pos]) : pos;
   const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -69,9 +85,21 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int qi = r * BLK + w * 32 + qn;
 
   // CSR bounds and block indices are wave-uniform: keep them in scalar registers
-  const int e0 = __builtin_amdgcn_readfirstlane(row_ptr[row]);
+  int e0 = __builtin_amdgcn_readfirstlane(row_ptr[row]);
   int e1 = __builtin_amdgcn_readfirstlane(row_ptr[row + 1]);
   if ((meta.skip_bits[h >> 5] >> (h & 31)) & 1u) e1 = e0;
+  // a long row is cut into near-equal chunks of at most split_blocks kept blocks
+  int n_chunks = 1;
+  if constexpr (kSplit) {
+    const int cnt = e1 - e0;
+    if (cnt > meta.split_blocks) n_chunks = (cnt + meta.split_blocks - 1) / meta.split_blocks;
+    if (chunk >= n_chunks) return;
+    if (n_chunks > 1) {
+      const int a0 = e0 + (int)(((long long)chunk * cnt) / n_chunks);
+      e1 = e0 + (int)(((long long)(chunk + 1) * cnt) / n_chunks);
+      e0 = a0;
+    }
+  }
 
   f32x16_t acc[kOut];
 #pragma unroll
@@ -273,6 +301,22 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
     l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
+  if (kSplit && n_chunks > 1) {
+    // one chunk of a split row: the unnormalised accumulator and (running max, sum) per
+    // query, merged into O by the combine kernel
+    if (qi < N) {
+      const size_t prow = ((size_t)chunk * total_rows + row) * BLK + (w * 32 + qn);
+      float* po = meta.part_o + prow * D;
+#pragma unroll
+      for (int io = 0; io < kOut; ++io)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(po + 32 * io + 8 * g + 4 * hf) =
+              make_float4(acc[io][4 * g + 0], acc[io][4 * g + 1], acc[io][4 * g + 2], acc[io][4 * g + 3]);
+      if (hf == 0) reinterpret_cast<float2*>(meta.part_ml)[prow] = make_float2(m_run, l_tot);
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // log of the softmax normaliser, natural units: the running max is in log2 units of the
   // scaled scores, l sums 2^(s*scale*log2e - max); -inf for an empty row
@@ -299,12 +343,70 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Merge the chunks of every split row: O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c with
+// M the largest chunk max; lse from M and the merged sum.  Rows that were not split were
+// finished by the attention kernel and are left alone.
+template <typename TO>
+__global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, int total_rows) {
+  const int row = blockIdx.x;
+  const int bh = row / a.Nb, r = row - bh * a.Nb, h = bh % a.H;
+  int cnt = a.row_ptr[row + 1] - a.row_ptr[row];
+  if ((a.skip_bits[h >> 5] >> (h & 31)) & 1u) cnt = 0;
+  if (cnt <= a.split_blocks) return;
+  const int n = (cnt + a.split_blocks - 1) / a.split_blocks;
+  const int blk = a.blk, D = a.d, C4 = D / 4;
+  const int nq = min(blk, a.N - r * blk);
+  const float4* po = reinterpret_cast<const float4*>(a.part_o);
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
+  TO* O = static_cast<TO*>(a.o);
+  for (int idx = threadIdx.x; idx < nq * C4; idx += 256) {
+    const int q = idx / C4, c4 = idx - q * C4;
+    float M = -INFINITY;
+    for (int c = 0; c < n; ++c) M = fmaxf(M, pml[((size_t)c * total_rows + row) * blk + q].x);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (M != -INFINITY) {
+      for (int c = 0; c < n; ++c) {
+        const size_t pr = ((size_t)c * total_rows + row) * blk + q;
+        const float2 ml = pml[pr];
+        if (ml.x == -INFINITY) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
+        const float4 v = po[pr * C4 + c4];
+        L = __builtin_fmaf(wgt, ml.y, L);
+        o.x = __builtin_fmaf(wgt, v.x, o.x);
+        o.y = __builtin_fmaf(wgt, v.y, o.y);
+        o.z = __builtin_fmaf(wgt, v.z, o.z);
+        o.w = __builtin_fmaf(wgt, v.w, o.w);
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const size_t qg = (size_t)bh * a.N + (size_t)r * blk + q;
+    TO* orow = O + qg * D + 4 * c4;
+    if constexpr (sizeof(TO) == 4) {
+      *reinterpret_cast<float4*>(orow) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(o.x * inv) | ((uint32_t)f32_to_bf16_rne(o.y * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(o.z * inv) | ((uint32_t)f32_to_bf16_rne(o.w * inv) << 16);
+      *reinterpret_cast<uint2*>(orow) = make_uint2(lo, hi);
+    }
+    if (c4 == 0 && a.lse) a.lse[qg] = (M + __log2f(L)) * 0.69314718055994531f;
+  }
+}
+
 template <typename T, typename TO, int D, int BLK>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t s) {
   const int total = a.B * a.H * a.Nb;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK>), dim3((unsigned)total), dim3(BLK * 2), 0, s,
-                     static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     static_cast<TO*>(a.o), a.row_ptr, a.col_idx, a.H, a.N, a.Nb, total, a.scale_log2, a);
+  if (a.split_blocks > 0) {
+    // 8 equal shares of (rows of the XCD's range) x (chunks per row)
+    const long long items = (long long)kXcds * ((total + kXcds - 1) / kXcds) * a.split_max;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2), 0, s,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<TO*>(a.o), a.row_ptr, a.col_idx, a.H, a.N, a.Nb, total, a.scale_log2, a);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK, false>), dim3((unsigned)total), dim3(BLK * 2), 0, s,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       static_cast<TO*>(a.o), a.row_ptr, a.col_idx, a.H, a.N, a.Nb, total, a.scale_log2, a);
+  }
   return hipGetLastError();
 }
 
@@ -317,6 +419,15 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_split_combine(const AttnArgs& a, hipStream_t s) {
+  const int total = a.B * a.H * a.Nb;
+  if (a.out_bf16)
+    hipLaunchKernelGGL(split_combine_kernel<uint16_t>, dim3((unsigned)total), dim3(256), 0, s, a, total);
+  else
+    hipLaunchKernelGGL(split_combine_kernel<float>, dim3((unsigned)total), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.in_bf16) {

@@ -115,7 +115,7 @@ typedef struct asa_csr {
 } asa_csr;
 
 /* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order;
- * 1.2.0 added asa_pattern_search. */
+ * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -212,6 +212,43 @@ asa_status asa_attention_fwd_lse(const void* Q, const void* K, const void* V, vo
                                  int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
                                  const asa_head_pattern* patterns, float scale, float* lse,
                                  void* stream);
+
+/* Workspace bytes for asa_attention_fwd_split with the same split_blocks: the chunk partials
+ * of split rows, split_max x B*H*Nb x blk x (d + 2) floats where split_max is the number of
+ * chunks a full row would get.  Returns 0 when the plan splits nothing (the workspace may
+ * then be NULL) or the arguments are invalid (the call reports which). */
+size_t asa_attention_fwd_split_workspace_size(const asa_shape* shape, int32_t split_blocks);
+
+/*
+ * asa_attention_fwd_split -- asa_attention_fwd with long rows split over several
+ * workgroups, for launches whose rows are few or uneven (few heads, short sequences, text
+ * rows or full heads beside sparse ones).
+ *
+ * Same result as asa_attention_fwd (Sparse-vDiT section 三 "核心公式", the masked
+ * attention), up to rounding: the pages fix no work decomposition.  A CSR row keeping
+ * more than T = split_blocks key blocks is cut into n = ceil(count / T) chunks of
+ * near-equal length (chunk c holds kept entries [c*count/n, (c+1)*count/n) of the row).
+ * Each chunk runs the online softmax over its blocks and leaves its unnormalised output
+ * and (running max, sum) per query in the workspace; a combine pass merges the chunks,
+ * O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c with M = max_c m_c.  Rows of at most
+ * T blocks are computed exactly as asa_attention_fwd computes them (bit-identical).
+ *
+ * split_blocks  T > 0, with ceil(Nb / T) <= 64; or 0 to choose T from the shape alone: a
+ *               launch of R < 384 rows (B*H*Nb; fewer than about 1.5 workgroups per compute
+ *               unit) gets T = max(16, ceil(Nb / ceil(384 / R))), so a row keeping every
+ *               block is cut into ceil(384 / R) chunks; launches of 384 rows or more are
+ *               not split.  When T >= Nb nothing is split and no workspace is needed.
+ * lse           device float32 [B,H,N] as asa_attention_fwd_lse, or NULL.
+ * workspace     device buffer of asa_attention_fwd_split_workspace_size() bytes, 256-byte
+ *               aligned (may be NULL when that size is 0).
+ * Other arguments and errors as asa_attention_fwd; a negative or too small split_blocks
+ * is ASA_ERR_BAD_PARAM.
+ */
+asa_status asa_attention_fwd_split(const void* Q, const void* K, const void* V, void* O,
+                                   int32_t o_dtype, const asa_shape* shape, const asa_csr* csr,
+                                   const asa_head_pattern* patterns, float scale, float* lse,
+                                   int32_t split_blocks, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Workspace bytes for asa_attention_bwd: the per-query (lse, D) pairs and the transposed
  * mask (key block -> query blocks), sized for the worst case B*H*Nb*Nb kept tiles.

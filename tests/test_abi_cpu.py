@@ -209,7 +209,37 @@ def test_pattern_search_rejects_arguments():
     assert _search(_shape(d=96)) == UNSUPPORTED
 
 
+def _split(s, T=4, ws=0x40000, ws_bytes=1 << 30, lse=None, csr=None):
+    csr = csr or _csr(asa.lib.asa_csr_capacity(ctypes.byref(s)))
+    return asa.lib.asa_attention_fwd_split(FAKE, FAKE, FAKE, FAKE, asa.ASA_F32, ctypes.byref(s), ctypes.byref(csr),
+                                           None, 0.0, lse, T, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_attention_split_rejects_arguments():
+    s = _shape()                                   # B1 H2 N1024 blk64: Nb 16, 32 rows
+    B, H, Nb, blk, d = 1, 2, 16, 64, 64
+    sz = lambda T: asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(s), T)
+    assert sz(4) >= 4 * B * H * Nb * blk * (d + 2) * 4     # 4 chunks per full row
+    assert sz(16) == 0 and sz(100) == 0                    # T >= Nb: nothing to split
+    assert sz(-1) == 0
+    assert sz(0) == 0                                      # 16-block rows: never split automatically
+    few = _shape(N=64 * 64)                                # 128 rows of 64 blocks: 3 chunks of 22
+    assert asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(few), 0) == \
+        asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(few), 22) > 0
+    many = _shape(N=64 * 192)                              # 384 rows: not split automatically
+    assert asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(many), 0) == 0
+    assert _split(s, T=-1) == BAD_PARAM
+    big = _shape(N=64 * 1000, blk=64)                      # Nb 1000: T=10 would make 100 chunks
+    assert _split(big, T=10) == BAD_PARAM
+    assert "chunks" in asa.lib.asa_last_error().decode()
+    assert _split(s, T=4, ws=0) == WORKSPACE
+    assert _split(s, T=4, ws_bytes=sz(4) - 1) == WORKSPACE
+    assert _split(s, T=4, ws=0x40010) == WORKSPACE
+    nullcsr = asa_csr(0, 0x30000, 10)
+    assert _split(s, csr=nullcsr) == NULL_ARG
+
+
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10200
+    assert asa.lib.asa_version() >= 10300
