@@ -14,6 +14,11 @@ What it computes, in the order the method applies it:
 * Static mask sources -- same page, the "四种注意力模式" table: M0 full,
   M1 skip (output set to zero), M2 diagonal (intra-frame), M3 multi-diagonal
   (evenly spaced diagonals, cross-frame), M4 vertical stripe (global tokens).
+  One more from "Efficient-vDiT: Efficient Video Diffusion Transformers With
+  Attention Tile", section 3.1 (注意力图块化): the 3D attention map splits into
+  frame-by-frame tiles that repeat, and a sparse tile set gives attention linear
+  in the number of frames.  The page names no tile set; the one here keeps, for
+  each query frame, its own frame and the first frame (frame tiles of F tokens).
 * Adaptive mask source -- BLADE ("BLADE: Block-Sparse Attention Meets Step
   Distillation for Efficient Video Generation"), abstract: ASA generates a
   content-aware block mask per input.  The pages give no rule, so this oracle
@@ -45,7 +50,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 # Integer codes shared with the C ABI by convention (each side defines them).
-ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE = 0, 1, 2, 3, 4, 5
+ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE, FRAME_TILE = 0, 1, 2, 3, 4, 5, 6
 TOPK, TAU = 0, 1
 
 AMBIGUITY_GAP = 1e-6
@@ -136,6 +141,8 @@ def static_row(pattern: int, param: int, r: int, N: int, blk: int) -> np.ndarray
     MULTIDIAG(S): tile (r, c) is kept iff some query i in block r and key j in
     block c satisfy (j - i) = 0 mod S, i.e. the integer interval
     [min T_c - max T_r, max T_c - min T_r] contains a multiple of S.
+    FRAME_TILE(F): with frame(t) = floor(t / F), tile (r, c) is kept iff some query i
+    in block r and key j in block c have frame(j) == frame(i) or frame(j) == 0.
     """
     Nb = num_blocks(N, blk)
     row = np.zeros(Nb, dtype=bool)
@@ -159,6 +166,16 @@ def static_row(pattern: int, param: int, r: int, N: int, blk: int) -> np.ndarray
             # smallest multiple of S that is >= lo, compared with hi
             first = -((-lo) // S) * S
             row[c] = first <= hi
+    elif pattern == FRAME_TILE:
+        F = int(param)
+        if F <= 0:
+            raise ValueError("frame-tile frame length must be positive")
+        qlo, qhi = block_range(r, N, blk)
+        qframes = set(range(qlo // F, (qhi - 1) // F + 1))
+        for c in range(Nb):
+            klo, khi = block_range(c, N, blk)
+            kframes = set(range(klo // F, (khi - 1) // F + 1))
+            row[c] = 0 in kframes or bool(qframes & kframes)
     else:
         raise ValueError(f"unknown pattern id {pattern}")
     return row

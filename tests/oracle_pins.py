@@ -264,6 +264,32 @@ def check_static_patterns_token_pairs():
             assert s2[:2].all() and not s2[2:].any()
 
 
+def check_frame_tile_token_pairs():
+    """Frame tiles (own frame + first frame) against token-pair enumeration, ragged blocks,
+    frame lengths that are and are not block multiples; F >= N is full attention and F = 1
+    is the diagonal plus the first key block."""
+    for N, blk in ((300, 32), (256, 64), (130, 16)):
+        Nb = O.num_blocks(N, blk)
+        i = np.arange(N)[:, None]
+        j = np.arange(N)[None, :]
+        for F in (1, 5, 32, 48, 100, 128):
+            tok = ((j // F) == (i // F)) | ((j // F) == 0)
+            for r in range(Nb):
+                ql, qh = O.block_range(r, N, blk)
+                want = np.array([tok[ql:qh, slice(*O.block_range(c, N, blk))].any() for c in range(Nb)])
+                assert np.array_equal(O.static_row(O.FRAME_TILE, F, r, N, blk), want), (N, blk, F, r)
+        for r in range(Nb):
+            assert O.static_row(O.FRAME_TILE, N, r, N, blk).all()
+            d1 = O.static_row(O.FRAME_TILE, 1, r, N, blk)
+            assert np.array_equal(d1, O.static_row(O.DIAG, 0, r, N, blk) | O.static_row(O.VSTRIPE, 1, r, N, blk))
+    # frames of 1024 tokens at N = 8192, blk 128: 8 blocks per frame, rows of frame f > 0
+    # keep their own 8 blocks and frame 0's 8
+    M = O.static_mask(1, 1, 8192, 128, [(O.FRAME_TILE, 1024)])
+    counts = M.sum(axis=-1)[0, 0]
+    assert (counts[:8] == 8).all() and (counts[8:] == 16).all()
+    assert abs(O.pattern_sparsity(O.FRAME_TILE, 1024, 8192, 128) - (1 - (8 * 1024 + 56 * 16 * 128) * 128 / 8192 ** 2)) < 1e-15
+
+
 def check_static_counts_8192():
     """Frame-stride multi-diagonal at N=8192, blk=128: 8 tiles per row; stripe 2; diag 1."""
     pats = [(O.DIAG, 0), (O.MULTIDIAG, 1024), (O.VSTRIPE, 2), (O.FULL, 0), (O.SKIP, 0)]
@@ -518,7 +544,8 @@ ALL_CHECKS = [
     check_attention_rows_match_full, check_pool_score_bilinearity,
     check_block_softmax_matches_scipy, check_rank_order_ties, check_selection_bruteforce,
     check_selection_limits_and_monotone, check_forced_blocks,
-    check_static_patterns_token_pairs, check_static_counts_8192, check_csr_layout,
+    check_static_patterns_token_pairs, check_frame_tile_token_pairs, check_static_counts_8192,
+    check_csr_layout,
     check_kept_tile_flops,
     check_bwd_finite_differences, check_bwd_matches_torch_autograd,
     check_bwd_identical_keys_closed_form, check_bwd_blocks_assemble_full, check_lse_matches_scipy,

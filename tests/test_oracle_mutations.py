@@ -88,6 +88,23 @@ def _static_floor(pattern, param, r, N, blk):
     return row
 
 
+def _frame_tile_variant(which):
+    def f(pattern, param, r, N, blk):
+        if pattern != core.FRAME_TILE:
+            return _orig_static(pattern, param, r, N, blk)
+        Nb = core.num_blocks(N, blk)
+        row = np.zeros(Nb, dtype=bool)
+        qlo, qhi = core.block_range(r, N, blk)
+        for c in range(Nb):
+            klo, khi = core.block_range(c, N, blk)
+            if which == "no_first_frame":
+                row[c] = klo // param <= (qhi - 1) // param and qlo // param <= (khi - 1) // param
+            else:   # frame of the block's end taken as qhi // F (one past the last token)
+                row[c] = klo < param or (klo // param <= qhi // param and qlo // param <= khi // param)
+        return row
+    return f
+
+
 def _row_attention_no_normalise(q, k, v):
     s = (q @ k.T) / np.sqrt(q.shape[-1])
     e = np.exp(s - s.max(axis=1, keepdims=True))
@@ -173,6 +190,8 @@ MUTATIONS = {
     "attention_missing_scale": ("_row_attention", _row_attention_noscale),
     "attention_drops_partial_key_block": ("kept_tokens", _kept_tokens_full_blocks_only),
     "multidiag_floor_not_ceiling": ("static_row", _static_floor),
+    "frame_tile_without_first_frame": ("static_row", _frame_tile_variant("no_first_frame")),
+    "frame_tile_end_off_by_one": ("static_row", _frame_tile_variant("end_off_by_one")),
     "attention_not_normalised": ("_row_attention", _row_attention_no_normalise),
     "bwd_dk_missing_scale": ("_row_attention_bwd", _bwd_variant("dk_missing_scale")),
     "bwd_ds_missing_rowsum": ("_row_attention_bwd", _bwd_variant("ds_missing_rowsum")),
