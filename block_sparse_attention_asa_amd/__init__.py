@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libasa.so")
 
 ASA_F32, ASA_BF16 = 0, 1
-ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE = 0, 1, 2, 3, 4, 5
+ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE, FRAME_TILE = 0, 1, 2, 3, 4, 5, 6
 TOPK, TAU = 0, 1
 
 
@@ -423,4 +423,4 @@ __all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attent
            "asa_attention_bwd", "asa_pattern_search",
            "asa_csr_capacity",
            "AsaError", "lib", "LIB_PATH", "EXPORTS", "num_blocks",
-           "ADAPTIVE", "FULL", "SKIP", "DIAG", "MULTIDIAG", "VSTRIPE", "TOPK", "TAU"]
+           "ADAPTIVE", "FULL", "SKIP", "DIAG", "MULTIDIAG", "VSTRIPE", "FRAME_TILE", "TOPK", "TAU"]

@@ -77,6 +77,9 @@ asa_status fill_heads(const asa_shape* s, const asa_head_pattern* pats, bool all
       case ASA_PAT_VSTRIPE:
         if (prm < 0) return fail(ASA_ERR_BAD_PATTERN, "head %d: vertical-stripe width %d must be >= 0", h, prm);
         break;
+      case ASA_PAT_FRAME_TILE:
+        if (prm <= 0) return fail(ASA_ERR_BAD_PATTERN, "head %d: frame-tile frame length %d must be > 0", h, prm);
+        break;
       default:
         return fail(ASA_ERR_BAD_PATTERN, "head %d: unknown pattern id %d", h, id);
     }
@@ -208,7 +211,7 @@ size_t split_workspace_layout(const asa_shape* s, int split_max, float** part_o,
 
 extern "C" {
 
-int32_t asa_version(void) { return 10300; }
+int32_t asa_version(void) { return 10400; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {
@@ -455,12 +458,14 @@ asa_status asa_pattern_search(const void* Q, const void* K, const void* V, const
   if (n_candidates > 0 && !candidates) return fail(ASA_ERR_NULL_ARG, "candidates is NULL");
   for (int i = 0; i < n_candidates; ++i) {
     const int id = candidates[i].id, prm = candidates[i].param;
-    if (id == ASA_PAT_ADAPTIVE || id < ASA_PAT_ADAPTIVE || id > ASA_PAT_VSTRIPE)
+    if (id == ASA_PAT_ADAPTIVE || id < ASA_PAT_ADAPTIVE || id > ASA_PAT_FRAME_TILE)
       return fail(ASA_ERR_BAD_PATTERN, "candidate %d: pattern id %d is not a static pattern", i, id);
     if (id == ASA_PAT_MULTIDIAG && prm <= 0)
       return fail(ASA_ERR_BAD_PATTERN, "candidate %d: multi-diagonal stride %d must be > 0", i, prm);
     if (id == ASA_PAT_VSTRIPE && prm < 0)
       return fail(ASA_ERR_BAD_PATTERN, "candidate %d: vertical-stripe width %d must be >= 0", i, prm);
+    if (id == ASA_PAT_FRAME_TILE && prm <= 0)
+      return fail(ASA_ERR_BAD_PATTERN, "candidate %d: frame-tile frame length %d must be > 0", i, prm);
   }
   if (!std::isfinite(lambda) || !std::isfinite(eps))
     return fail(ASA_ERR_BAD_PARAM, "lambda and eps must be finite");

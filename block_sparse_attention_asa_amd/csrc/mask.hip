@@ -58,6 +58,15 @@ __device__ inline bool static_keep(int id, int param, int r, int c, int N, int b
       const long long S = param;
       return floor_div(hi, S) * S >= lo;                // a multiple of S lies in [lo, hi]
     }
+    case 6: {  // frame tiles of `param` tokens: the query's own frames and frame 0
+      const long long F = param;
+      const long long qlo = (long long)r * blk;
+      const long long qhi = min(qlo + blk, (long long)N) - 1;
+      const long long klo = (long long)c * blk;
+      const long long khi = min(klo + blk, (long long)N) - 1;
+      if (klo < F) return true;                         // the block holds frame-0 keys
+      return klo / F <= qhi / F && qlo / F <= khi / F;  // frame ranges overlap
+    }
     default:  // skip, adaptive
       return false;
   }

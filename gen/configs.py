@@ -16,7 +16,7 @@ from typing import List, Optional, Tuple
 
 # pattern ids (Sparse-vDiT, "四种注意力模式" table: M0 full, M1 skip, M2 diagonal,
 # M3 multi-diagonal, M4 vertical stripe; 0 = the adaptive ASA source)
-ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE = 0, 1, 2, 3, 4, 5
+ADAPTIVE, FULL, SKIP, DIAG, MULTIDIAG, VSTRIPE, FRAME_TILE = 0, 1, 2, 3, 4, 5, 6
 TOPK, TAU = 0, 1
 
 

@@ -56,8 +56,8 @@ typedef enum asa_status {
 
 typedef enum asa_dtype { ASA_F32 = 0, ASA_BF16 = 1 } asa_dtype;
 
-/* Per-head mask sources.  Codes follow the Sparse-vDiT mode table (M0..M4) plus the
- * adaptive ASA source. */
+/* Per-head mask sources.  Codes follow the Sparse-vDiT mode table (M0..M4), plus the
+ * adaptive ASA source and Efficient-vDiT's frame tiles. */
 enum {
   ASA_PAT_ADAPTIVE = 0,   /* adaptive only (asa_build_mask)                                 */
   ASA_PAT_FULL = 1,       /* M0: every key block                                           */
@@ -65,7 +65,13 @@ enum {
   ASA_PAT_DIAG = 3,       /* M2: key block c == query block r                              */
   ASA_PAT_MULTIDIAG = 4,  /* M3: param = stride S in tokens (> 0); tile (r,c) kept iff some
                              query i in block r and key j in block c have (j - i) % S == 0  */
-  ASA_PAT_VSTRIPE = 5     /* M4: param = s >= 0 leading key blocks (global tokens), c < s   */
+  ASA_PAT_VSTRIPE = 5,    /* M4: param = s >= 0 leading key blocks (global tokens), c < s   */
+  ASA_PAT_FRAME_TILE = 6  /* frame tiles, after "Efficient-vDiT: Efficient Video Diffusion
+                             Transformers With Attention Tile", section 3.1: param = F > 0
+                             tokens per frame, frame(t) = floor(t / F); tile (r,c) kept iff
+                             some query i in block r and key j in block c have
+                             frame(j) == frame(i) or frame(j) == 0.  The page names no tile
+                             set; this one (own frame + first frame) costs O(N F).        */
 };
 
 enum { ASA_MODE_TOPK = 0, ASA_MODE_TAU = 1 };
@@ -115,7 +121,8 @@ typedef struct asa_csr {
 } asa_csr;
 
 /* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order;
- * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split. */
+ * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split; 1.4.0 added
+ * ASA_PAT_FRAME_TILE. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */

@@ -113,6 +113,12 @@ def test_static_mask_rejects_arguments():
     assert call(ctypes.byref(s), good, ctypes.byref(csr), ctypes.c_void_p(0x40000), 8, None) == WORKSPACE
     nullcsr = asa_csr(0, 0x30000, cap)
     assert call(ctypes.byref(s), good, ctypes.byref(nullcsr), ctypes.c_void_p(0x40000), 1 << 30, None) == NULL_ARG
+    for bad_f in (0, -5):
+        tile = (asa_head_pattern * 2)(asa_head_pattern(asa.FRAME_TILE, bad_f), asa_head_pattern(asa.FULL, 0))
+        assert call(ctypes.byref(s), tile, ctypes.byref(csr), ctypes.c_void_p(0x40000), 1 << 30, None) == BAD_PATTERN
+        assert "frame-tile" in asa.lib.asa_last_error().decode()
+    unknown = (asa_head_pattern * 2)(asa_head_pattern(7, 1), asa_head_pattern(asa.FULL, 0))
+    assert call(ctypes.byref(s), unknown, ctypes.byref(csr), ctypes.c_void_p(0x40000), 1 << 30, None) == BAD_PATTERN
 
 
 def test_attention_rejects_arguments():
@@ -200,6 +206,7 @@ def test_pattern_search_rejects_arguments():
     assert _search(s, cands=[(asa.SKIP, 0), (asa.MULTIDIAG, 0)]) == BAD_PATTERN
     assert _search(s, cands=[(asa.VSTRIPE, -1)]) == BAD_PATTERN
     assert _search(s, cands=[(11, 0)]) == BAD_PATTERN
+    assert _search(s, cands=[(asa.FRAME_TILE, 0)]) == BAD_PATTERN
     assert _search(s, lam=float("inf")) == BAD_PARAM
     assert _search(s, eps=float("nan")) == BAD_PARAM
     assert _search(s, scale=float("nan")) == BAD_PARAM
@@ -242,4 +249,4 @@ def test_attention_split_rejects_arguments():
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10300
+    assert asa.lib.asa_version() >= 10400
