@@ -12,7 +12,7 @@
 //
 // Pipeline (all on the caller's stream):
 //   pool_kernel      Q, K -> Qp [B,H,Nb,d], KpT [B,H,d,Nb] (float64 means); HBM-bound.
-//   score_kernel     S = Qp KpT / sqrt(d), 32 x 32 tiles through LDS, 2 x 2 per thread.
+//   score_kernel     S = Qp KpT / sqrt(d) on the fp64 matrix cores, 32 x 32 tiles.
 //   select_kernel    one workgroup per row: softmax, bitonic sort of (P, c) held in
 //                    registers (cross-lane, LDS or in-register exchanges), prefix
 //                    selection, union with forced / static blocks -> bitmask.
@@ -105,8 +105,9 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
         acc[2 * j + 1] += bf16_to_f64((uint16_t)(w[j] >> 16));
       }
     };
-    // rows in the same order as one at a time, but a batch of loads in flight at once
-    constexpr int kBatch = 4;
+    // rows in the same order as one at a time, but all of a thread's loads for a full
+    // 128-token block in flight at once
+    constexpr int kBatch = 128 / RPP;
     int i = sub;
     for (; i + (kBatch - 1) * RPP < n; i += kBatch * RPP) {
       uint4 v[kBatch];
@@ -149,66 +150,46 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 }
 
 // ------------------------------------------------------------------ block scores
-// One workgroup computes a 32 x 32 tile of S for one head: query blocks r0.., key blocks
-// c0...  The pooled rows are staged through LDS in 32-wide slices of d; each thread owns a
-// 2 x 2 sub-tile (rows tr + 16i, columns tc + 16j) and accumulates in float64 in a fixed
-// order over d.  grid = B*H * ceil(Nb/32)^2, enough workgroups to fill the GPU even for a
-// few heads.
+// S = Qp KpT / sqrt(d) for one head, a dense float64 contraction, on the fp64 matrix cores
+// (v_mfma_f64_16x16x4f64).  One workgroup computes a 32 x 32 tile of S (query blocks r0..,
+// key blocks c0..); each of its four wavefronts owns a 16 x 16 quarter.  Operand layout of
+// the instruction, per lane l: A holds row l%16, k = l/16; B holds k = l/16, column l%16;
+// result component e holds row 4e + l/16, column l%16.  Two accumulators take alternate
+// k-steps.  grid = B*H * ceil(Nb/32)^2.
 constexpr int kST = 32;          // score tile edge
-constexpr int kSD = 32;          // d slice
-constexpr int kSP = kST / 16;    // outputs per thread along each tile edge
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qp,
                                                          const double* __restrict__ kpt,
                                                          double* __restrict__ score, int Nb) {
-  __shared__ double qs[kST][kSD + 1];
-  __shared__ double ks[kSD][kST + 1];
   const int tiles = (Nb + kST - 1) / kST;
   int id = blockIdx.x;
   const int tcol = id % tiles;
   id /= tiles;
   const int trow = id % tiles, bh = id / tiles;
-  const int r0 = trow * kST, c0 = tcol * kST;
-  const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int r0 = trow * kST + 16 * (w >> 1), c0 = tcol * kST + 16 * (w & 1);
+  const int ra = r0 + (l & 15), kl = l >> 4, cb = c0 + (l & 15);
   const double* q = qp + (size_t)bh * Nb * D;
   const double* kt = kpt + (size_t)bh * D * Nb;
-  double acc[kSP][kSP];
-#pragma unroll
-  for (int i = 0; i < kSP; ++i)
-#pragma unroll
-    for (int j = 0; j < kSP; ++j) acc[i][j] = 0.0;
-  for (int d0 = 0; d0 < D; d0 += kSD) {
-#pragma unroll
-    for (int e = tid; e < kST * kSD; e += kThreads) {
-      const int rr = e / kSD, dd = e - rr * kSD;            // q: row-major, d fastest
-      qs[rr][dd] = r0 + rr < Nb ? q[(size_t)(r0 + rr) * D + d0 + dd] : 0.0;
-      const int d2 = e / kST, cc = e - d2 * kST;            // k: transposed, block fastest
-      ks[d2][cc] = c0 + cc < Nb ? kt[(size_t)(d0 + d2) * Nb + c0 + cc] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < kSD; ++dd) {
-      double qv[kSP], kv[kSP];
-#pragma unroll
-      for (int i = 0; i < kSP; ++i) qv[i] = qs[tr + 16 * i][dd];
-#pragma unroll
-      for (int j = 0; j < kSP; ++j) kv[j] = ks[dd][tc + 16 * j];
-#pragma unroll
-      for (int i = 0; i < kSP; ++i)
-#pragma unroll
-        for (int j = 0; j < kSP; ++j) acc[i][j] = fma(qv[i], kv[j], acc[i][j]);
-    }
-    __syncthreads();
+  const bool a_ok = ra < Nb, b_ok = cb < Nb;
+  f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int k0 = 0; k0 < D; k0 += 8) {
+    const double a0 = a_ok ? q[(size_t)ra * D + k0 + kl] : 0.0;
+    const double b0 = b_ok ? kt[(size_t)(k0 + kl) * Nb + cb] : 0.0;
+    const double a1 = a_ok ? q[(size_t)ra * D + k0 + 4 + kl] : 0.0;
+    const double b1 = b_ok ? kt[(size_t)(k0 + 4 + kl) * Nb + cb] : 0.0;
+    acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc1, 0, 0, 0);
   }
   const double sqrt_d = sqrt((double)D);
+  const int c = c0 + (l & 15);
+  if (c < Nb) {
 #pragma unroll
-  for (int i = 0; i < kSP; ++i) {
-    const int r = r0 + tr + 16 * i;
-    if (r >= Nb) continue;
-#pragma unroll
-    for (int j = 0; j < kSP; ++j) {
-      const int c = c0 + tc + 16 * j;
-      if (c < Nb) score[((size_t)bh * Nb + r) * Nb + c] = acc[i][j] / sqrt_d;
+    for (int e = 0; e < 4; ++e) {
+      const int r = r0 + 4 * e + (l >> 4);
+      if (r < Nb) score[((size_t)bh * Nb + r) * Nb + c] = (acc0[e] + acc1[e]) / sqrt_d;
     }
   }
 }
@@ -268,19 +249,30 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
   }
   if (r < p.n_text_blocks) {   // query block holding text tokens: full row
     for (int c = tid; c < Nb; c += kThreads) atomicOr(&word[c >> 5], 1u << (c & 31));
+  } else if (p.mode == 0 && p.k >= Nb) {   // top-k keeping every block: nothing to rank
+    for (int c = tid; c < Nb; c += kThreads) atomicOr(&word[c >> 5], 1u << (c & 31));
   } else {
-    // softmax over all key blocks of this row
     const double* srow = score + (size_t)row * Nb;
-    double mx = -INFINITY;
-    for (int c = tid; c < Nb; c += kThreads) mx = fmax(mx, srow[c]);
-    mx = block_reduce_max(mx, scratch);
-    double part = 0.0;
-    for (int c = tid; c < Nb; c += kThreads) {
-      const double e = exp(srow[c] - mx);
-      key[c] = e;
-      part += e;
+    // Rank keys.  Top-k ranks by the score itself: exp is increasing, so the order by P
+    // equals the order by S wherever the S values differ by more than float64 rounding of
+    // P can hide (a top-k boundary closer than that is a near-tie, see ambiguous rows).
+    // The mass prefix needs P itself: softmax over all key blocks of this row.
+    double z = 1.0;
+    if (p.mode == 0) {
+      for (int c = tid; c < Nb; c += kThreads) key[c] = srow[c];
+      __syncthreads();
+    } else {
+      double mx = -INFINITY;
+      for (int c = tid; c < Nb; c += kThreads) mx = fmax(mx, srow[c]);
+      mx = block_reduce_max(mx, scratch);
+      double part = 0.0;
+      for (int c = tid; c < Nb; c += kThreads) {
+        const double e = exp(srow[c] - mx);
+        key[c] = e;
+        part += e;
+      }
+      z = block_reduce_sum(part, scratch);   // also a barrier for key[]
     }
-    const double z = block_reduce_sum(part, scratch);   // also a barrier for key[]
     // Bitonic sort of (P, c) into rank order over np2 = 2^ceil(log2 Nb) slots.  Slot
     // i = e*kThreads + tid lives in register e of thread tid.  A compare-exchange at
     // distance j runs across lanes of one wavefront (j < 64, no barrier), through LDS
@@ -293,7 +285,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int i = e * kThreads + tid;
-      kv[e] = i < Nb ? key[i] / z : -1.0;   // padding ranks after every real block
+      // padding ranks after every real block (scores are finite, weights >= 0)
+      kv[e] = i < Nb ? (p.mode == 0 ? key[i] : key[i] / z) : (p.mode == 0 ? -INFINITY : -1.0);
       ki[e] = i < Nb ? i : 0x7fffffff;
     }
     // keep the first-ranked of (a, b) when `first`, else the other one
