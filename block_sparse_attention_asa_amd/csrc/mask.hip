@@ -194,9 +194,71 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restric
   }
 }
 
-// (p, c) comes before (q, e) in rank order: larger probability first, then smaller block.
-__device__ inline bool ranks_before(double p, int c, double q, int e) {
-  return p > q || (p == q && c < e);
+// Rank keys.  Rank order is value descending, then block index ascending.  A key packs
+// both into one uint64: the value's bits made order-preserving as an unsigned integer,
+// its lowest 10 bits replaced by 1023 - c.  Dropping those bits merges values closer than
+// 2^-42 relative (far inside the near-tie gap, where rows are ambiguous anyway); every
+// other pair of blocks keeps its order, and keys of distinct blocks never tie.  Padding
+// slots get key 0, after every real block.
+__device__ inline uint64_t rank_key(double v, int c) {
+  uint64_t b = (uint64_t)__double_as_longlong(v);
+  b = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+  return (b & ~(uint64_t)0x3FF) | (uint64_t)(1023 - c);
+}
+__device__ inline int key_block(uint64_t k) { return 1023 - (int)(k & 0x3FF); }
+
+// Bitonic sort, keys descending, over NP2 slots: slot i = e*kThreads + tid lives in
+// register e of thread tid.  A compare-exchange at distance j runs inside a thread's
+// registers (j >= kThreads), through LDS (64 <= j < kThreads, two barriers) or across the
+// lanes of one wavefront (j < 64, no barrier).  Every stage is unrolled, so each branch
+// below is resolved at compile time.
+template <int NP2, int KK, int J>
+__device__ inline void bitonic_stage(uint64_t* kv, uint64_t* lds) {
+  constexpr int PER = (NP2 + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  if constexpr (J >= kThreads) {
+    constexpr int je = J / kThreads;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int e2 = e ^ je;
+      if (e2 > e) {
+        const int i = e * kThreads + tid;
+        const bool desc = (i & KK) == 0;   // this pair's run sorts descending
+        const uint64_t a = kv[e], b = kv[e2];
+        if ((a > b) != desc) { kv[e] = b; kv[e2] = a; }
+      }
+    }
+  } else if constexpr (J >= 64) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) lds[e * kThreads + tid] = kv[e];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = e * kThreads + tid;
+      const uint64_t b = lds[i ^ J];
+      const bool first = ((i & KK) == 0) == ((i & J) == 0);   // keep the higher-ranked one
+      kv[e] = first ? (kv[e] > b ? kv[e] : b) : (kv[e] > b ? b : kv[e]);
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = e * kThreads + tid;
+      const uint64_t b = (uint64_t)__shfl_xor((long long)kv[e], J, 64);
+      const bool first = ((i & KK) == 0) == ((i & J) == 0);
+      kv[e] = first ? (kv[e] > b ? kv[e] : b) : (kv[e] > b ? b : kv[e]);
+    }
+  }
+  if constexpr (J > 1) bitonic_stage<NP2, KK, J / 2>(kv, lds);
+}
+template <int NP2, int KK>
+__device__ inline void bitonic_pass(uint64_t* kv, uint64_t* lds) {
+  bitonic_stage<NP2, KK, KK / 2>(kv, lds);
+  if constexpr (KK < NP2) bitonic_pass<NP2, KK * 2>(kv, lds);
+}
+template <int NP2>
+__device__ inline void bitonic_sort_desc(uint64_t* kv, uint64_t* lds) {
+  if constexpr (NP2 >= 2) bitonic_pass<NP2, 2>(kv, lds);
 }
 
 // ------------------------------------------------------------------ block reductions
@@ -227,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
                                                           int32_t* __restrict__ count,
                                                           MaskGeom g, AdaptiveParams p,
                                                           HeadTable heads) {
-  __shared__ double key[kMaxMaskBlocks];
-  __shared__ int idx[kMaxMaskBlocks];
+  __shared__ double wgt[kMaxMaskBlocks];     // scores (top-k) or softmax numerators (mass)
+  __shared__ uint64_t xch[kMaxMaskBlocks];   // sort exchange space, then the ranked blocks
   __shared__ double scratch[kThreads];
   __shared__ uint32_t word[kMaxMaskBlocks / 32];
   __shared__ int kept_prefix;
@@ -259,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
     // The mass prefix needs P itself: softmax over all key blocks of this row.
     double z = 1.0;
     if (p.mode == 0) {
-      for (int c = tid; c < Nb; c += kThreads) key[c] = srow[c];
+      for (int c = tid; c < Nb; c += kThreads) wgt[c] = srow[c];
       __syncthreads();
     } else {
       double mx = -INFINITY;
@@ -268,91 +330,49 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
       double part = 0.0;
       for (int c = tid; c < Nb; c += kThreads) {
         const double e = exp(srow[c] - mx);
-        key[c] = e;
+        wgt[c] = e;
         part += e;
       }
-      z = block_reduce_sum(part, scratch);   // also a barrier for key[]
+      z = block_reduce_sum(part, scratch);   // also a barrier for wgt[]
     }
-    // Bitonic sort of (P, c) into rank order over np2 = 2^ceil(log2 Nb) slots.  Slot
-    // i = e*kThreads + tid lives in register e of thread tid.  A compare-exchange at
-    // distance j runs across lanes of one wavefront (j < 64, no barrier), through LDS
-    // (64 <= j < kThreads), or between a thread's own registers (j >= kThreads).
     int np2 = 1;
     while (np2 < Nb) np2 <<= 1;
     constexpr int kPer = kMaxMaskBlocks / kThreads;
-    double kv[kPer];
-    int ki[kPer];
+    uint64_t kv[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int i = e * kThreads + tid;
-      // padding ranks after every real block (scores are finite, weights >= 0)
-      kv[e] = i < Nb ? (p.mode == 0 ? key[i] : key[i] / z) : (p.mode == 0 ? -INFINITY : -1.0);
-      ki[e] = i < Nb ? i : 0x7fffffff;
+      kv[e] = i < Nb ? rank_key(p.mode == 0 ? wgt[i] : wgt[i] / z, i) : 0ull;
     }
-    // keep the first-ranked of (a, b) when `first`, else the other one
-    auto pick = [](double& a, int& ia, double b, int ib, bool first) {
-      const bool a_first = ranks_before(a, ia, b, ib);
-      if (a_first != first) { a = b; ia = ib; }
-    };
-    for (int kk = 2; kk <= np2; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        if (j >= kThreads) {
-          const int je = j / kThreads;
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) {
-            const int e2 = e ^ je;
-            if (e2 > e && e2 < kPer) {
-              const int i = e * kThreads + tid;
-              const bool up = (i & kk) == 0;
-              double a = kv[e], b = kv[e2];
-              int ia = ki[e], ib = ki[e2];
-              if (ranks_before(a, ia, b, ib) != up) {
-                kv[e] = b; ki[e] = ib; kv[e2] = a; ki[e2] = ia;
-              }
-            }
-          }
-        } else if (j >= 64) {
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) {
-            if (e * kThreads < np2) { key[e * kThreads + tid] = kv[e]; idx[e * kThreads + tid] = ki[e]; }
-          }
-          __syncthreads();
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) {
-            const int i = e * kThreads + tid;
-            if (e * kThreads < np2) {
-              const int pi = i ^ j;
-              pick(kv[e], ki[e], key[pi], idx[pi], ((i & kk) == 0) == ((i & j) == 0));
-            }
-          }
-          __syncthreads();
-        } else {
-#pragma unroll
-          for (int e = 0; e < kPer; ++e) {
-            if (e * kThreads < np2) {   // workgroup-uniform
-              const int i = e * kThreads + tid;
-              const double b = __shfl_xor(kv[e], j, 64);
-              const int ib = __shfl_xor(ki[e], j, 64);
-              pick(kv[e], ki[e], b, ib, ((i & kk) == 0) == ((i & j) == 0));
-            }
-          }
-        }
-      }
+    switch (np2) {
+      case 1: break;
+      case 2: bitonic_sort_desc<2>(kv, xch); break;
+      case 4: bitonic_sort_desc<4>(kv, xch); break;
+      case 8: bitonic_sort_desc<8>(kv, xch); break;
+      case 16: bitonic_sort_desc<16>(kv, xch); break;
+      case 32: bitonic_sort_desc<32>(kv, xch); break;
+      case 64: bitonic_sort_desc<64>(kv, xch); break;
+      case 128: bitonic_sort_desc<128>(kv, xch); break;
+      case 256: bitonic_sort_desc<256>(kv, xch); break;
+      case 512: bitonic_sort_desc<512>(kv, xch); break;
+      default: bitonic_sort_desc<1024>(kv, xch); break;
     }
     // length of the adaptive prefix
     if (p.mode == 0) {
       if (tid == 0) kept_prefix = min(max(p.k, 0), Nb);
     } else {
-      // running mass summed sequentially in rank order (the order fixes the float64 bits)
+      // running mass in rank order, summed sequentially from the exact weights (the order
+      // fixes the float64 bits): the ranked block indices go through LDS
+      int* order_lds = reinterpret_cast<int*>(xch);   // free again after the sort
 #pragma unroll
       for (int e = 0; e < kPer; ++e)
-        if (e * kThreads < np2) key[e * kThreads + tid] = kv[e];
+        if (e * kThreads < np2) order_lds[e * kThreads + tid] = key_block(kv[e]);
       __syncthreads();
       if (tid == 0) {
         int m = Nb;
         double mass = 0.0;
         for (int t = 0; t < Nb; ++t) {
-          mass += key[t];
+          mass += wgt[order_lds[t]] / z;
           if (mass >= p.tau) { m = t + 1; break; }
         }
         if (p.k_cap > 0) m = min(m, p.k_cap);
@@ -364,7 +384,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const double* __restri
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int i = e * kThreads + tid;
-      if (i < m) atomicOr(&word[ki[e] >> 5], 1u << (ki[e] & 31));
+      if (i < m) {
+        const int c = key_block(kv[e]);
+        atomicOr(&word[c >> 5], 1u << (c & 31));
+      }
     }
     for (int c = tid; c < Nb; c += kThreads) {
       const bool forced = (p.keep_diag && c == r) || (c < p.n_text_blocks) ||
