@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
   constexpr int VEC = 8;
   constexpr int TPR = D / VEC;          // threads per token row
   constexpr int RPP = kThreads / TPR;   // token rows per pass
-  __shared__ double red[kThreads][VEC + 1];
+  __shared__ double red[RPP][D];        // per-thread partial sums, one row per row group
 
   const int row = blockIdx.x;
   const int bh = row / Nb, r = row - bh * Nb;
@@ -128,24 +128,15 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
     }
   }
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) red[t][j] = acc[j];
+  for (int j = 0; j < VEC; ++j) red[sub][col + j] = acc[j];
   __syncthreads();
-  for (int s = RPP / 2; s > 0; s >>= 1) {   // fixed-order tree: deterministic
-    if (sub < s) {
+  if (t < D) {   // one thread per column sums the row groups in a fixed order
+    double v = 0.0;
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) red[t][j] += red[t + s * TPR][j];
-    }
-    __syncthreads();
-  }
-  if (sub == 0) {
-    const double inv_n = (double)n;
-    if (blockIdx.y == 0) {
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) qp[(size_t)row * D + col + j] = red[t][j] / inv_n;
-    } else {
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) kpt[((size_t)bh * D + col + j) * Nb + r] = red[t][j] / inv_n;
-    }
+    for (int s = 0; s < RPP; ++s) v += red[s][t];
+    const double nn = (double)n;
+    if (blockIdx.y == 0) qp[(size_t)row * D + t] = v / nn;
+    else kpt[((size_t)bh * D + t) * Nb + r] = v / nn;
   }
 }
 
