@@ -170,9 +170,11 @@ asa::AttnArgs attn_args(const void* Q, const void* K, const void* V, void* O, bo
 // Split-row plan: chunk length T (kept blocks per workgroup) and chunks per row at most.
 // split_blocks = 0 chooses T from the shape: a launch of fewer than kSplitRows rows (about
 // 1.5 workgroups per compute unit) leaves compute units idle, so each row is cut into
-// ceil(kSplitRows / rows) chunks, none shorter than kMinChunk blocks (shorter chunks cost
-// more in partial outputs than they gain).  A plan that can never split a row returns 0.
+// ceil(kSplitItems / rows) chunks (two workgroups per compute unit), none shorter than
+// kMinChunk blocks (shorter chunks cost more in partial outputs than they gain).  A plan
+// that can never split a row returns 0.
 constexpr int64_t kSplitRows = 384;
+constexpr int64_t kSplitItems = 512;
 constexpr int64_t kMinChunk = 16;
 
 int split_plan(const asa_shape* s, int32_t split_blocks, int* split_max) {
@@ -184,7 +186,7 @@ int split_plan(const asa_shape* s, int32_t split_blocks, int* split_max) {
       *split_max = 1;
       return 0;
     }
-    const int64_t n = (kSplitRows + rows - 1) / rows;
+    const int64_t n = (kSplitItems + rows - 1) / rows;
     t = (Nb + n - 1) / n;
     if (t < kMinChunk) t = kMinChunk;
     const int64_t floor_t = (Nb + asa::kMaxSplit - 1) / asa::kMaxSplit;

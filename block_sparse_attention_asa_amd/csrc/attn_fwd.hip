@@ -345,10 +345,13 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 
 // Merge the chunks of every split row: O = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c with
 // M the largest chunk max; lse from M and the merged sum.  Rows that were not split were
-// finished by the attention kernel and are left alone.
+// finished by the attention kernel and are left alone.  One workgroup per 32 queries of a
+// row (grid = rows * blk / 32).
+constexpr int kCombineQ = 32;
 template <typename TO>
 __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, int total_rows) {
-  const int row = blockIdx.x;
+  const int qs = a.blk / kCombineQ;
+  const int row = blockIdx.x / qs, q0 = (blockIdx.x - row * qs) * kCombineQ;
   const int bh = row / a.Nb, r = row - bh * a.Nb, h = bh % a.H;
   int cnt = a.row_ptr[row + 1] - a.row_ptr[row];
   if ((a.skip_bits[h >> 5] >> (h & 31)) & 1u) cnt = 0;
@@ -356,11 +359,13 @@ __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, int tota
   const int n = (cnt + a.split_blocks - 1) / a.split_blocks;
   const int blk = a.blk, D = a.d, C4 = D / 4;
   const int nq = min(blk, a.N - r * blk);
+  if (q0 >= nq) return;
+  const int qn = min(kCombineQ, nq - q0);
   const float4* po = reinterpret_cast<const float4*>(a.part_o);
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
   TO* O = static_cast<TO*>(a.o);
-  for (int idx = threadIdx.x; idx < nq * C4; idx += 256) {
-    const int q = idx / C4, c4 = idx - q * C4;
+  for (int idx = threadIdx.x; idx < qn * C4; idx += 256) {
+    const int q = q0 + idx / C4, c4 = idx % C4;
     float M = -INFINITY;
     for (int c = 0; c < n; ++c) M = fmaxf(M, pml[((size_t)c * total_rows + row) * blk + q].x);
     float L = 0.f;
@@ -422,10 +427,11 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_split_combine(const AttnArgs& a, hipStream_t s) {
   const int total = a.B * a.H * a.Nb;
+  const dim3 grid((unsigned)(total * (a.blk / kCombineQ)));
   if (a.out_bf16)
-    hipLaunchKernelGGL(split_combine_kernel<uint16_t>, dim3((unsigned)total), dim3(256), 0, s, a, total);
+    hipLaunchKernelGGL(split_combine_kernel<uint16_t>, grid, dim3(256), 0, s, a, total);
   else
-    hipLaunchKernelGGL(split_combine_kernel<float>, dim3((unsigned)total), dim3(256), 0, s, a, total);
+    hipLaunchKernelGGL(split_combine_kernel<float>, grid, dim3(256), 0, s, a, total);
   return hipGetLastError();
 }
 

@@ -241,10 +241,10 @@ size_t asa_attention_fwd_split_workspace_size(const asa_shape* shape, int32_t sp
  * T blocks are computed exactly as asa_attention_fwd computes them (bit-identical).
  *
  * split_blocks  T > 0, with ceil(Nb / T) <= 64; or 0 to choose T from the shape alone: a
- *               launch of R < 384 rows (B*H*Nb; fewer than about 1.5 workgroups per compute
- *               unit) gets T = max(16, ceil(Nb / ceil(384 / R))), so a row keeping every
- *               block is cut into ceil(384 / R) chunks; launches of 384 rows or more are
- *               not split.  When T >= Nb nothing is split and no workspace is needed.
+ *               launch of R < 384 rows (B*H*Nb; fewer than about 1.5 workgroups per
+ *               compute unit) gets T = max(16, ceil(Nb / ceil(512 / R))), so a row keeping
+ *               every block is cut into ceil(512 / R) chunks (two per compute unit);
+ *               launches of 384 rows or more are not split.  When T >= Nb nothing is split and no workspace is needed.
  * lse           device float32 [B,H,N] as asa_attention_fwd_lse, or NULL.
  * workspace     device buffer of asa_attention_fwd_split_workspace_size() bytes, 256-byte
  *               aligned (may be NULL when that size is 0).

@@ -230,9 +230,9 @@ def test_attention_split_rejects_arguments():
     assert sz(16) == 0 and sz(100) == 0                    # T >= Nb: nothing to split
     assert sz(-1) == 0
     assert sz(0) == 0                                      # 16-block rows: never split automatically
-    few = _shape(N=64 * 64)                                # 128 rows of 64 blocks: 3 chunks of 22
+    few = _shape(N=64 * 64)                                # 128 rows of 64 blocks: 4 chunks of 16
     assert asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(few), 0) == \
-        asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(few), 22) > 0
+        asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(few), 16) > 0
     many = _shape(N=64 * 192)                              # 384 rows: not split automatically
     assert asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(many), 0) == 0
     assert _split(s, T=-1) == BAD_PARAM
