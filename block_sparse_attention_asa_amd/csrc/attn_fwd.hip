@@ -8,11 +8,12 @@
 // "四种注意力模式" table) produce zeros.
 //
 // Work decomposition: one workgroup per (b, h, query block r); BLK/32 wavefronts, each
-// owning 32 query rows.  For every kept key block the workgroup stages K (row-major) and
-// V (transposed, key-permuted) in LDS, then each wavefront computes
+// owning 32 query rows.  Kept key blocks are consumed in 64-key steps: K and V of a step
+// land row-major (16-byte granules swizzled) in one slot of a two-slot LDS ring by direct
+// global -> LDS transfers, and each wavefront computes
 //     S^T = K_c Q^T          (32x32x16 bf16 MFMA, or 32x32x2 f32 MFMA for fp32 inputs)
 //     online softmax          (exp2 with the scale folded in, running max / sum per row)
-//     O^T += V_c^T P^T        (same MFMA shape)
+//     O^T += V_c^T P^T        (same MFMA shape; V^T fragments by transpose reads)
 // Computing the transposed products makes every lane own one query row: the S^T
 // accumulator layout puts 16 keys of query (lane % 32) in each lane, and the O^T layout
 // puts 16 output columns of the same query there, so the softmax statistics and the
