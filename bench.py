@@ -63,11 +63,24 @@ def cpu_baseline(cfg, x, budget_s):
     import numpy as np
     import gen
     import oracle as O
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     q64, k64, v64 = (gen.as_float64(x[n]) for n in ("q", "k", "v"))
     t0 = time.perf_counter()
     M = O.build_mask(q64, k64, cfg.blk, mode=cfg.mode, k=cfg.k, keep_diag=cfg.keep_diag)
@@ -97,6 +110,8 @@ def cpu_baseline(cfg, x, budget_s):
                    f"attention on {blocks} of {cfg.B * cfg.H * cfg.Nb} query blocks drawn over all heads ({t_att:.2f} s), "
                    f"extrapolated by kept-tile flops to one step ({t_step:.1f} s)"),
         "step_seconds_extrapolated": t_step,
+        "cpu_model": cpu_model,
+        "blas": blas,
     }
 
 
@@ -172,12 +187,30 @@ def main():
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    mask_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
-    attn_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
+    mask_t = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
+    attn_t = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+    step_t = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)])
+    mask_ms, attn_ms = float(mask_t.mean()), float(attn_t.mean())
+    pct = lambda a: [round(float(np.percentile(a, q)), 4) for q in (10, 50, 90)]
     step_ms_ev = float(np.mean([ev[i][0].elapsed_time(ev[i][2]) for i in range(args.steps)]))
     ms_per_step = wall * 1e3 / args.steps
 
-    result_extra = {}
+    result_extra = {"attn_ms_p10_p50_p90": pct(attn_t), "mask_ms_p10_p50_p90": pct(mask_t),
+                    "step_ms_p10_p50_p90": pct(step_t)}
+    if args.calib_copy == 0:
+        # measured HBM ceiling: device-to-device copies of 1 GiB (read + write); left out of
+        # counter runs, whose only copy is the calibration copy
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        cev[0].record(stream)
+        for _ in range(3):
+            dst.copy_(src)
+        cev[1].record(stream)
+        torch.cuda.synchronize()
+        result_extra["hbm_copy_gbs"] = round(3 * 2 * float(1 << 30) / (cev[0].elapsed_time(cev[1]) / 1e3) / 1e9, 1)
+        del src, dst
     if not args.no_dense:
         log("bench: dense all-ones run of the same kernel")
         drp, dci = asa.asa_static_mask(B, H, N, blk, [(asa.FULL, 0)] * H, dev)
