@@ -537,6 +537,38 @@ def check_select_rule_cases():
     assert np.allclose(L, [[0.011, 0.025]], rtol=0, atol=1e-15)
 
 
+def check_search_follows_table3_trends():
+    """The page's Table 3 (tests/golden/sparse_vdit_table3.json): a larger epsilon or a
+    smaller lambda gives a larger speedup, i.e. sparser choices.  On heads whose losses
+    spread across the thresholds (uniform attention, Q = 0, so each output row is a mean of
+    V), the oracle's kept fraction of token pairs must order the settings the same way."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "sparse_vdit_table3.json")
+    rows = json.load(open(path))["rows"]
+    B, H, N, d, blk = 1, 12, 320, 8, 64                 # 5 blocks
+    rng = RNG(47)
+    q = np.zeros((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    offs = rng.standard_normal((B, H, 5, d))
+    v = np.repeat(offs, blk, axis=2) + 0.3 * rng.standard_normal((B, H, N, d))
+    v *= np.geomspace(0.1, 0.8, H)[None, :, None, None]    # pattern losses from ~0.01 to ~0.7
+    v += 1.0                                               # large outputs: skipping never pays
+    cands = [(O.SKIP, 0), (O.DIAG, 0), (O.VSTRIPE, 3)]
+    kept = {}
+    for row in rows:
+        choice, L, mse, S = O.pattern_search(q, k, v, blk, cands, row["lambda"], row["epsilon"])
+        dens = np.array([1.0] + [1.0 - x for x in S])         # choice 0 = full attention
+        kept[(row["lambda"], row["epsilon"])] = float(dens[choice].mean())
+    for a in rows:
+        for b in rows:
+            if a["speedup"] > b["speedup"]:
+                ka, kb = kept[(a["lambda"], a["epsilon"])], kept[(b["lambda"], b["epsilon"])]
+                assert ka <= kb, (a, b, ka, kb)
+    # epsilon alone moves the choice on these heads
+    assert kept[(0.01, 0.15)] < kept[(0.01, 0.1)] < kept[(0.01, 0.05)], kept
+
+
 ALL_CHECKS = [
     check_dense_equals_sdpa, check_block_diagonal_equals_independent_blocks,
     check_weights_sum_to_one, check_identical_keys_give_mean_of_v,
@@ -551,4 +583,5 @@ ALL_CHECKS = [
     check_bwd_identical_keys_closed_form, check_bwd_blocks_assemble_full, check_lse_matches_scipy,
     check_pattern_sparsity_token_pairs, check_pattern_mse_matches_torch,
     check_pattern_uniform_attention_closed_form, check_select_rule_cases,
+    check_search_follows_table3_trends,
 ]

@@ -16,6 +16,8 @@ The search is checked link by link:
      wherever that tolerance cannot change the decision; other heads are logged as
      ambiguous, and each case may hold only a few.
 """
+import json
+import os
 from dataclasses import replace
 
 import numpy as np
@@ -28,7 +30,9 @@ from gpu_helpers import BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, csr_to_device,
 
 pytestmark = pytest.mark.gpu
 
-LAM, EPS = 0.01, 0.1      # the page's Table 3 setting
+# the page's default setting: the first row of its Table 3 (tests/golden/sparse_vdit_table3.json)
+_T3 = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "sparse_vdit_table3.json")))
+LAM, EPS = _T3["rows"][0]["lambda"], _T3["rows"][0]["epsilon"]
 
 
 def _cands(cfg):
