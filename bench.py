@@ -126,6 +126,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward (training) timing")
     ap.add_argument("--no-search", action="store_true", help="skip the per-head pattern search timing")
     ap.add_argument("--no-split", action="store_true", help="skip the split-row timing (one head in full)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -197,6 +198,30 @@ def main():
 
     result_extra = {"attn_ms_p10_p50_p90": pct(attn_t), "mask_ms_p10_p50_p90": pct(mask_t),
                     "step_ms_p10_p50_p90": pct(step_t)}
+    if not args.no_graph:
+        # the same step captured once in a HIP graph and replayed (no host launches)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            build_mask()
+            attend(row_ptr, col_idx, out, order)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            build_mask()
+            attend(row_ptr, col_idx, out, order)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        result_extra["graph_ms_per_step"] = round(gms, 4)
+        result_extra["graph_value"] = round(flops / gms / 1e9, 2)
+        del graph
     if args.calib_copy == 0:
         # measured HBM ceiling: device-to-device copies of 1 GiB (read + write); left out of
         # counter runs, whose only copy is the calibration copy
