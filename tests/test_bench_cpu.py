@@ -31,13 +31,18 @@ def test_kept_tile_flops_matches_the_oracle_count():
 
 def test_traffic_record_is_ignored_when_the_sources_change(tmp_path, monkeypatch):
     import json
+    import hashlib
     rec = json.load(open(os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")))
-    assert bench.load_traffic("attn_fwd_wan") == rec["bytes_per_launch"]
-    # the same sources under another root: reported while the hash matches, not after a change
+    # the sources under another root, with a record made for them: reported while the hash
+    # matches, not after a change
+    h = hashlib.sha256()
     for rel in rec["sources"]:
         dst = tmp_path / rel
         dst.parent.mkdir(parents=True, exist_ok=True)
-        dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
+        data = open(os.path.join(ROOT, rel), "rb").read()
+        dst.write_bytes(data)
+        h.update(data)
+    rec["source_sha256"] = h.hexdigest()
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "attn_fwd_wan_traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
