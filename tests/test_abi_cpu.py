@@ -246,6 +246,36 @@ def test_attention_split_rejects_arguments():
     assert _split(s, csr=nullcsr) == NULL_ARG
 
 
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "asa.h"
+int main(void) {
+  asa_shape s = {1, 2, 1024, 64, 64, ASA_BF16};
+  if (asa_version() < 10400) return 1;
+  if (asa_csr_capacity(&s) != 2 * 16 * 16) return 2;
+  asa_status st = asa_attention_fwd(NULL, NULL, NULL, NULL, ASA_F32, &s, NULL, NULL, 0.0f, NULL);
+  if (st != ASA_ERR_NULL_ARG) return 3;
+  if (strlen(asa_last_error()) == 0) return 4;
+  printf("%s\n", asa_status_string(st));
+  return 0;
+}
+"""
+
+
+def test_plain_c_client_links_and_calls(tmp_path):
+    """The header and the library are usable from plain C (no Python, no GPU work)."""
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(asa.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe),
+                    f"-L{libdir}", "-lasa", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, (res.returncode, res.stderr)
+    assert res.stdout.strip() == "ASA_ERR_NULL_ARG"
+
+
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
