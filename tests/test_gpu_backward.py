@@ -189,3 +189,57 @@ def test_backward_full_size_sampled(asa_lib):
     _compare_grad(torch.from_numpy(np.concatenate(got_q)), np.concatenate(ref_q), "dQ sampled")
     _compare_grad(torch.from_numpy(np.concatenate(got_k)), np.concatenate(ref_k), "dK sampled")
     _compare_grad(torch.from_numpy(np.concatenate(got_v)), np.concatenate(ref_v), "dV sampled")
+
+
+def test_backward_full_size_720p_sampled(asa_lib):
+    """720p-like layer at full size (B=1, H=24, N=75600, d=128: Nb = 591, last block 80
+    tokens; adaptive top-30 unioned with a one-frame multi-diagonal; heads 22-23 skipped):
+    the largest mask the builders take in the workloads.  Sampled query blocks (dQ) and key
+    blocks (dK, dV) against the oracle; skipped heads must be exactly zero."""
+    asa = asa_lib
+    cfg = gen.LONG720
+    say(f"case {cfg.name}: full-size backward, sampled")
+    x = gen.make_inputs(cfg)
+    q64, k64, v64 = (gen.as_float64(x[n]) for n in ("q", "k", "v"))
+    M = _oracle_mask(cfg, q64, k64)
+    Meff = M.copy()
+    for h, (pid, _) in enumerate(cfg.patterns):
+        if pid == O.SKIP:
+            Meff[:, h] = False
+    xd = to_device(x)
+    rp, ci = csr_to_device(M)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
+    o = asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp, ci, cfg.blk, patterns=cfg.patterns, lse=lse)
+    dout = _dout((cfg.B, cfg.H, cfg.N, cfg.d), 8)
+    dq, dk, dv = asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], o, dout.to("cuda:0"), lse, rp, ci, cfg.blk,
+                                       patterns=cfg.patterns)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert torch.all(t[:, 22:] == 0), "skipped heads must have zero gradients"
+    g64 = dout.to(torch.float64).numpy()
+    rng = np.random.default_rng(720)
+    Nb, N = cfg.Nb, cfg.N
+    got_q, ref_q, got_k, ref_k, got_v, ref_v = [], [], [], [], [], []
+    for h in (0, 13, 21):
+        dq_h, dk_h, dv_h = (t[0, h].cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+        for r in sorted(set(rng.integers(0, Nb, 2).tolist()) | {Nb - 1}):
+            lo, hi = O.block_range(r, N, cfg.blk)
+            a, _, _, _ = O.attention_bwd_block(q64, k64, v64, g64, Meff, cfg.blk, 0, h, r)
+            got_q.append(dq_h[lo:hi])
+            ref_q.append(a)
+        for c in sorted(set(rng.integers(0, Nb, 1).tolist()) | {Nb - 1}):
+            klo, khi = O.block_range(c, N, cfg.blk)
+            sk = np.zeros((khi - klo, cfg.d))
+            sv = np.zeros((khi - klo, cfg.d))
+            for r in np.nonzero(Meff[0, h, :, c])[0]:
+                _, J, bk, bv = O.attention_bwd_block(q64, k64, v64, g64, Meff, cfg.blk, 0, h, int(r))
+                sel = (J >= klo) & (J < khi)
+                sk[J[sel] - klo] += bk[sel]
+                sv[J[sel] - klo] += bv[sel]
+            got_k.append(dk_h[klo:khi])
+            ref_k.append(sk)
+            got_v.append(dv_h[klo:khi])
+            ref_v.append(sv)
+    _compare_grad(torch.from_numpy(np.concatenate(got_q)), np.concatenate(ref_q), "dQ sampled")
+    _compare_grad(torch.from_numpy(np.concatenate(got_k)), np.concatenate(ref_k), "dK sampled")
+    _compare_grad(torch.from_numpy(np.concatenate(got_v)), np.concatenate(ref_v), "dV sampled")
