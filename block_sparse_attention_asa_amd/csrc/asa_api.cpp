@@ -286,8 +286,7 @@ asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if ((e = asa::launch_pool(Q, K, shape->in_dtype == ASA_BF16, g, ws, s)) != hipSuccess) return hip_fail(e, "pool");
-  if ((e = asa::launch_scores(g, ws, s)) != hipSuccess) return hip_fail(e, "scores");
-  if ((e = asa::launch_select(g, p, heads, ws, s)) != hipSuccess) return hip_fail(e, "select");
+  if ((e = asa::launch_rank(g, p, heads, ws, s)) != hipSuccess) return hip_fail(e, "rank");
   if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, out->order, s)) != hipSuccess) return hip_fail(e, "csr");
   return ASA_OK;
 }

@@ -40,7 +40,6 @@ struct AdaptiveParams {
 struct MaskWorkspace {
   double* qp;      // [B*H*Nb*d]  pooled queries, row-major
   double* kpt;     // [B*H*d*Nb]  pooled keys, transposed per head
-  double* score;   // [B*H*Nb*Nb] block scores
   uint32_t* bits;  // [B*H*Nb*words] kept-block bitmask per row
   int32_t* count;  // [B*H*Nb] kept blocks per row
 };
@@ -50,9 +49,8 @@ size_t mask_workspace_layout(const MaskGeom& g, bool adaptive, MaskWorkspace* ws
 // Mask pipeline stages (enqueue only; return the launch status).
 hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& g,
                        const MaskWorkspace& ws, hipStream_t s);
-hipError_t launch_scores(const MaskGeom& g, const MaskWorkspace& ws, hipStream_t s);
-hipError_t launch_select(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
-                         const MaskWorkspace& ws, hipStream_t s);
+hipError_t launch_rank(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
+                       const MaskWorkspace& ws, hipStream_t s);
 hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const MaskWorkspace& ws,
                               hipStream_t s);
 hipError_t launch_csr(const MaskGeom& g, const MaskWorkspace& ws, int32_t* row_ptr,

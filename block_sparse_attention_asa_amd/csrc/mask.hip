@@ -12,10 +12,11 @@
 //
 // Pipeline (all on the caller's stream):
 //   pool_kernel      Q, K -> Qp [B,H,Nb,d], KpT [B,H,d,Nb] (float64 means); HBM-bound.
-//   score_kernel     S = Qp KpT / sqrt(d) on the fp64 matrix cores, 32 x 32 tiles.
-//   select_kernel    one workgroup per row: softmax, bitonic sort of (P, c) held in
-//                    registers (cross-lane, LDS or in-register exchanges), prefix
-//                    selection, union with forced / static blocks -> bitmask.
+//   rank_kernel      one workgroup per 16 rows of a head: S = Qp KpT / sqrt(d) on the
+//                    fp64 matrix cores into LDS, then per row (one wavefront for 4 rows)
+//                    the softmax where needed, a bitonic sort of the packed rank keys in
+//                    registers, prefix selection and the union with forced / static
+//                    blocks -> bitmask and count.
 //   static_kernel    one wavefront per row: static pattern bitmask only.
 //   csr_scan_kernel  exclusive scan of per-row counts -> row_ptr; optionally the
 //                    processing order (long rows first inside each XCD range).
@@ -140,57 +141,33 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
   }
 }
 
-// ------------------------------------------------------------------ block scores
-// S = Qp KpT / sqrt(d) for one head, a dense float64 contraction, on the fp64 matrix cores
-// (v_mfma_f64_16x16x4f64).  One workgroup computes a 32 x 32 tile of S (query blocks r0..,
-// key blocks c0..); each of its four wavefronts owns a 16 x 16 quarter.  Operand layout of
-// the instruction, per lane l: A holds row l%16, k = l/16; B holds k = l/16, column l%16;
-// result component e holds row 4e + l/16, column l%16.  Two accumulators take alternate
-// k-steps.  grid = B*H * ceil(Nb/32)^2.
-constexpr int kST = 32;          // score tile edge
+// ------------------------------------------------------------------ block scores + selection
+// One workgroup owns kRankRows consecutive query-block rows of one head.
+//
+// Scores: S = Qp KpT / sqrt(d) for those rows against all Nb key blocks, a dense float64
+// contraction on the fp64 matrix cores (v_mfma_f64_16x16x4f64), written to LDS.  Operand
+// layout of the instruction, per lane l: A holds row l%16, k = l/16; B holds k = l/16,
+// column l%16; result component e holds row 4e + l/16, column l%16.  The A operand (the
+// rows' pooled queries) stays in registers while the wavefronts take 16-column tiles
+// in turn, with two accumulators on alternate k-steps.
+//
+// Selection: each of the eight wavefronts ranks kRankRowsPerWave rows.  Rank order is value
+// descending, then block index ascending, and a key packs both into one uint64: the
+// value's bits made order-preserving as an unsigned integer, its lowest 10 bits replaced
+// by 1023 - c.  Dropping those bits merges values closer than 2^-42 relative (far inside
+// the near-tie gap, where rows are ambiguous anyway); every other pair of blocks keeps its
+// order, and keys of distinct blocks never tie.  Padding slots get key 0, after every
+// real block.  Slot i of a row lives in register i % PER of lane i / PER (PER = NP2 / 64).
+// Top-k needs only the k-th largest key (select_kth).  The mass prefix needs the rank
+// order: a bitonic network sorts the NP2 slots, where exchanges at distance J < PER stay
+// inside a lane's registers and the others cross lanes at distance J / PER; RI rows go
+// through the network side by side for instruction-level parallelism.
+constexpr int kRankRows = 16;
+constexpr int kRankThreads = 512;   // two wavefronts per SIMD
+constexpr int kRankWaves = kRankThreads / 64;
+constexpr int kRankRowsPerWave = kRankRows / kRankWaves;
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
-template <int D>
-__global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qp,
-                                                         const double* __restrict__ kpt,
-                                                         double* __restrict__ score, int Nb) {
-  const int tiles = (Nb + kST - 1) / kST;
-  int id = blockIdx.x;
-  const int tcol = id % tiles;
-  id /= tiles;
-  const int trow = id % tiles, bh = id / tiles;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int r0 = trow * kST + 16 * (w >> 1), c0 = tcol * kST + 16 * (w & 1);
-  const int ra = r0 + (l & 15), kl = l >> 4, cb = c0 + (l & 15);
-  const double* q = qp + (size_t)bh * Nb * D;
-  const double* kt = kpt + (size_t)bh * D * Nb;
-  const bool a_ok = ra < Nb, b_ok = cb < Nb;
-  f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-  for (int k0 = 0; k0 < D; k0 += 8) {
-    const double a0 = a_ok ? q[(size_t)ra * D + k0 + kl] : 0.0;
-    const double b0 = b_ok ? kt[(size_t)(k0 + kl) * Nb + cb] : 0.0;
-    const double a1 = a_ok ? q[(size_t)ra * D + k0 + 4 + kl] : 0.0;
-    const double b1 = b_ok ? kt[(size_t)(k0 + 4 + kl) * Nb + cb] : 0.0;
-    acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, acc1, 0, 0, 0);
-  }
-  const double sqrt_d = sqrt((double)D);
-  const int c = c0 + (l & 15);
-  if (c < Nb) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = r0 + 4 * e + (l >> 4);
-      if (r < Nb) score[((size_t)bh * Nb + r) * Nb + c] = (acc0[e] + acc1[e]) / sqrt_d;
-    }
-  }
-}
 
-// Rank keys.  Rank order is value descending, then block index ascending.  A key packs
-// both into one uint64: the value's bits made order-preserving as an unsigned integer,
-// its lowest 10 bits replaced by 1023 - c.  Dropping those bits merges values closer than
-// 2^-42 relative (far inside the near-tie gap, where rows are ambiguous anyway); every
-// other pair of blocks keeps its order, and keys of distinct blocks never tie.  Padding
-// slots get key 0, after every real block.
 __device__ inline uint64_t rank_key(double v, int c) {
   uint64_t b = (uint64_t)__double_as_longlong(v);
   b = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
@@ -198,200 +175,291 @@ __device__ inline uint64_t rank_key(double v, int c) {
 }
 __device__ inline int key_block(uint64_t k) { return 1023 - (int)(k & 0x3FF); }
 
-// Bitonic sort, keys descending, over NP2 slots: slot i = e*kThreads + tid lives in
-// register e of thread tid.  A compare-exchange at distance j runs inside a thread's
-// registers (j >= kThreads), through LDS (64 <= j < kThreads, two barriers) or across the
-// lanes of one wavefront (j < 64, no barrier).  Every stage is unrolled, so each branch
-// below is resolved at compile time.
-template <int NP2, int KK, int J>
-__device__ inline void bitonic_stage(uint64_t* kv, uint64_t* lds) {
-  constexpr int PER = (NP2 + kThreads - 1) / kThreads;
-  const int tid = threadIdx.x;
-  if constexpr (J >= kThreads) {
-    constexpr int je = J / kThreads;
+// Compare-exchange stages J, J/2, .., 1 of the merge of runs of KK slots (runs whose index
+// has bit KK clear sort descending).  Each exchange is one 64-bit compare and two selects:
+// a slot takes its partner's key when the compare disagrees with the slot's role.
+template <int PER, int RI, int KK, int J>
+__device__ inline void rank_stage(uint64_t (&kv)[RI][PER], int lane) {
+  if constexpr (J < PER) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int e2 = e ^ je;
-      if (e2 > e) {
-        const int i = e * kThreads + tid;
-        const bool desc = (i & KK) == 0;   // this pair's run sorts descending
-        const uint64_t a = kv[e], b = kv[e2];
-        if ((a > b) != desc) { kv[e] = b; kv[e2] = a; }
+      if ((e ^ J) > e) {
+        const bool desc = ((lane * PER + e) & KK) == 0;
+#pragma unroll
+        for (int j = 0; j < RI; ++j) {
+          const uint64_t a = kv[j][e], b = kv[j][e ^ J];
+          const bool sw = (a < b) == desc;
+          kv[j][e] = sw ? b : a;
+          kv[j][e ^ J] = sw ? a : b;
+        }
       }
     }
-  } else if constexpr (J >= 64) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) lds[e * kThreads + tid] = kv[e];
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int i = e * kThreads + tid;
-      const uint64_t b = lds[i ^ J];
-      const bool first = ((i & KK) == 0) == ((i & J) == 0);   // keep the higher-ranked one
-      kv[e] = first ? (kv[e] > b ? kv[e] : b) : (kv[e] > b ? b : kv[e]);
-    }
-    __syncthreads();
   } else {
+    constexpr int LJ = J / PER;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int i = e * kThreads + tid;
-      const uint64_t b = (uint64_t)__shfl_xor((long long)kv[e], J, 64);
-      const bool first = ((i & KK) == 0) == ((i & J) == 0);
-      kv[e] = first ? (kv[e] > b ? kv[e] : b) : (kv[e] > b ? b : kv[e]);
+      const int i = lane * PER + e;
+      const bool hi = ((i & KK) == 0) == ((i & J) == 0);   // this slot keeps the larger key
+#pragma unroll
+      for (int j = 0; j < RI; ++j) {
+        const uint64_t a = kv[j][e];
+        const uint64_t b = (uint64_t)__shfl_xor((long long)a, LJ, 64);
+        const bool keep = (a > b) == hi;
+        kv[j][e] = keep ? a : b;
+      }
     }
   }
-  if constexpr (J > 1) bitonic_stage<NP2, KK, J / 2>(kv, lds);
+  if constexpr (J > 1) rank_stage<PER, RI, KK, J / 2>(kv, lane);
 }
-template <int NP2, int KK>
-__device__ inline void bitonic_pass(uint64_t* kv, uint64_t* lds) {
-  bitonic_stage<NP2, KK, KK / 2>(kv, lds);
-  if constexpr (KK < NP2) bitonic_pass<NP2, KK * 2>(kv, lds);
-}
-template <int NP2>
-__device__ inline void bitonic_sort_desc(uint64_t* kv, uint64_t* lds) {
-  if constexpr (NP2 >= 2) bitonic_pass<NP2, 2>(kv, lds);
+template <int PER, int RI, int NP2, int KK>
+__device__ inline void rank_sort_desc(uint64_t (&kv)[RI][PER], int lane) {
+  rank_stage<PER, RI, KK, KK / 2>(kv, lane);
+  if constexpr (KK < NP2) rank_sort_desc<PER, RI, NP2, KK * 2>(kv, lane);
 }
 
-// ------------------------------------------------------------------ block reductions
-// Workgroup reductions: butterfly within each wavefront, then the 4 wave results in a fixed
-// order (deterministic).  scratch holds at least 4 doubles.
-__device__ inline double block_reduce_max(double v, double* scratch) {
+__device__ inline double wave_max(double v) {
   for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const double r = fmax(fmax(scratch[0], scratch[1]), fmax(scratch[2], scratch[3]));
-  __syncthreads();
-  return r;
+  return v;
 }
-
-__device__ inline double block_reduce_sum(double v, double* scratch) {
+__device__ inline double wave_sum(double v) {   // butterfly: every lane gets the same bits
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const double r = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
-  __syncthreads();
-  return r;
+  return v;
+}
+__device__ inline int wave_min_int(int v) {
+  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
+  return v;
 }
 
-// ------------------------------------------------------------------ selection
-// grid = B*H*Nb rows; one workgroup per row.
-__global__ __launch_bounds__(kThreads) void select_kernel(const double* __restrict__ score,
-                                                          uint32_t* __restrict__ bits,
-                                                          int32_t* __restrict__ count,
-                                                          MaskGeom g, AdaptiveParams p,
-                                                          HeadTable heads) {
-  __shared__ double wgt[kMaxMaskBlocks];     // scores (top-k) or softmax numerators (mass)
-  __shared__ uint64_t xch[kMaxMaskBlocks];   // sort exchange space, then the ranked blocks
-  __shared__ double scratch[kThreads];
-  __shared__ uint32_t word[kMaxMaskBlocks / 32];
-  __shared__ int kept_prefix;
+__device__ inline uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
 
-  const int row = blockIdx.x;
-  const int bh = row / g.Nb, r = row - bh * g.Nb, h = bh % g.H;
-  const int tid = threadIdx.x;
-  const int pid = heads.id[h], prm = heads.param[h];
+// The m-th largest key of a row held by one wavefront (slot e of each lane; `real` marks
+// the lanes whose slot e holds a block; real keys are distinct; 1 <= m <= real count).
+// Each round reads one candidate as the pivot (from the first slot holding candidates, the
+// first candidate lane at or after a rotating lane, so that an order of the keys by block
+// index cannot force many rounds), counts the
+// candidates above it with ballots, and keeps the side that holds the answer.  A round
+// returns or removes the pivot from the candidates, and the rank sought stays >= 1, so the
+// rounds are bounded by candidates + m; the loop bound enforces that.
+template <int PER>
+__device__ inline uint64_t select_kth(const uint64_t (&kv)[PER], const uint64_t (&real)[PER], int m) {
+  uint64_t cand[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) cand[e] = real[e];
+  int r = m;
+  uint64_t piv = 0;
+  for (int it = 0; it < 2 * 64 * PER + 2; ++it) {
+    const int o = (it * 37) & 63;
+    int esel = PER;
+    uint64_t msk = 0ull;
+#pragma unroll
+    for (int e = PER - 1; e >= 0; --e)
+      if (cand[e] != 0ull) { esel = e; msk = cand[e]; }
+    if (esel == PER) break;   // no candidate left (only for keys that are not distinct)
+    const uint64_t rot = o ? ((msk >> o) | (msk << (64 - o))) : msk;
+    const int lsel = (__ffsll((unsigned long long)rot) - 1 + o) & 63;
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (e == esel) piv = readlane64(kv[e], lsel);
+    uint64_t gt[PER];
+    int above = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      gt[e] = __ballot(kv[e] > piv) & cand[e];
+      above += __popcll(gt[e]);
+    }
+    if (above == r - 1) return piv;
+    if (above >= r) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) cand[e] = gt[e];
+    } else {
+      r -= above + 1;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) cand[e] &= __ballot(kv[e] < piv);
+    }
+  }
+  return piv;
+}
+
+// grid = B*H*ceil(Nb/kRankRows) workgroups; NP2 = max(64, Nb rounded up to a power of two).
+// The ids an XCD receives map onto one contiguous range of row tiles, so the tiles of a
+// head (which all read that head's KpT) share an L2.
+template <int D, int NP2>
+__global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __restrict__ qp,
+                                                        const double* __restrict__ kpt,
+                                                        uint32_t* __restrict__ bits,
+                                                        int32_t* __restrict__ count, MaskGeom g,
+                                                        AdaptiveParams p, HeadTable heads) {
+  constexpr int PER = NP2 / 64;
+  constexpr int RI = PER >= 16 ? 1 : 2;
+  static_assert(kRankRowsPerWave % RI == 0, "rows per wavefront split into equal passes");
+  __shared__ double srow[kRankRows][NP2];
+  __shared__ uint32_t word[kRankRows][kMaxMaskBlocks / 32];
+
   const int Nb = g.Nb;
+  const int tiles = (Nb + kRankRows - 1) / kRankRows;
+  int lo, hi;
+  xcd_range((int)(blockIdx.x % kXcds), g.B * g.H * tiles, lo, hi);
+  const int tile = lo + (int)(blockIdx.x / kXcds);
+  const int bh = tile / tiles, r0 = (tile - bh * tiles) * kRankRows, h = bh % g.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int pid = heads.id[h], prm = heads.param[h];
+  const size_t row0 = (size_t)bh * Nb + r0;
+  const int nrows = min(kRankRows, Nb - r0);
 
-  if (tid < g.words) word[tid] = 0u;
-  __syncthreads();
-
-  if (pid == 2) {   // skip head: empty row
-    if (tid < g.words) bits[(size_t)row * g.words + tid] = 0u;
-    if (tid == 0) count[row] = 0;
+  if (pid == 2) {   // skip head: empty rows
+    for (int i = tid; i < nrows * g.words; i += kRankThreads) bits[row0 * g.words + i] = 0u;
+    if (tid < nrows) count[row0 + tid] = 0;
     return;
   }
-  if (r < p.n_text_blocks) {   // query block holding text tokens: full row
-    for (int c = tid; c < Nb; c += kThreads) atomicOr(&word[c >> 5], 1u << (c & 31));
-  } else if (p.mode == 0 && p.k >= Nb) {   // top-k keeping every block: nothing to rank
-    for (int c = tid; c < Nb; c += kThreads) atomicOr(&word[c >> 5], 1u << (c & 31));
-  } else {
-    const double* srow = score + (size_t)row * Nb;
-    // Rank keys.  Top-k ranks by the score itself: exp is increasing, so the order by P
-    // equals the order by S wherever the S values differ by more than float64 rounding of
-    // P can hide (a top-k boundary closer than that is a near-tie, see ambiguous rows).
-    // The mass prefix needs P itself: softmax over all key blocks of this row.
-    double z = 1.0;
-    if (p.mode == 0) {
-      for (int c = tid; c < Nb; c += kThreads) wgt[c] = srow[c];
-      __syncthreads();
-    } else {
-      double mx = -INFINITY;
-      for (int c = tid; c < Nb; c += kThreads) mx = fmax(mx, srow[c]);
-      mx = block_reduce_max(mx, scratch);
-      double part = 0.0;
-      for (int c = tid; c < Nb; c += kThreads) {
-        const double e = exp(srow[c] - mx);
-        wgt[c] = e;
-        part += e;
-      }
-      z = block_reduce_sum(part, scratch);   // also a barrier for wgt[]
-    }
-    int np2 = 1;
-    while (np2 < Nb) np2 <<= 1;
-    constexpr int kPer = kMaxMaskBlocks / kThreads;
-    uint64_t kv[kPer];
+  for (int i = tid; i < kRankRows * (kMaxMaskBlocks / 32); i += kRankThreads) (&word[0][0])[i] = 0u;
+
+  {  // scores of the tile's rows
+    // Rows past Nb and columns past Nb read clamped (valid) addresses: they only feed
+    // outputs that are never used, and unconditional loads can all be in flight at once.
+    const double* q = qp + (size_t)bh * Nb * D;
+    const double* kt = kpt + (size_t)bh * D * Nb;
+    const int ra = min(r0 + (lane & 15), Nb - 1), kl = lane >> 4;
+    double a[D / 4], b[D / 4];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = e * kThreads + tid;
-      kv[e] = i < Nb ? rank_key(p.mode == 0 ? wgt[i] : wgt[i] / z, i) : 0ull;
-    }
-    switch (np2) {
-      case 1: break;
-      case 2: bitonic_sort_desc<2>(kv, xch); break;
-      case 4: bitonic_sort_desc<4>(kv, xch); break;
-      case 8: bitonic_sort_desc<8>(kv, xch); break;
-      case 16: bitonic_sort_desc<16>(kv, xch); break;
-      case 32: bitonic_sort_desc<32>(kv, xch); break;
-      case 64: bitonic_sort_desc<64>(kv, xch); break;
-      case 128: bitonic_sort_desc<128>(kv, xch); break;
-      case 256: bitonic_sort_desc<256>(kv, xch); break;
-      case 512: bitonic_sort_desc<512>(kv, xch); break;
-      default: bitonic_sort_desc<1024>(kv, xch); break;
-    }
-    // length of the adaptive prefix
-    if (p.mode == 0) {
-      if (tid == 0) kept_prefix = min(max(p.k, 0), Nb);
-    } else {
-      // running mass in rank order, summed sequentially from the exact weights (the order
-      // fixes the float64 bits): the ranked block indices go through LDS
-      int* order_lds = reinterpret_cast<int*>(xch);   // free again after the sort
+    for (int s = 0; s < D / 4; ++s) a[s] = q[(size_t)ra * D + 4 * s + kl];
+    const double sqrt_d = sqrt((double)D);
+    const int ctiles = (Nb + 15) / 16;
+    for (int ct = w; ct < ctiles; ct += kRankWaves) {
+      const int c = ct * 16 + (lane & 15);
+      const int cc = min(c, Nb - 1);
 #pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        if (e * kThreads < np2) order_lds[e * kThreads + tid] = key_block(kv[e]);
-      __syncthreads();
-      if (tid == 0) {
-        int m = Nb;
-        double mass = 0.0;
-        for (int t = 0; t < Nb; ++t) {
-          mass += wgt[order_lds[t]] / z;
-          if (mass >= p.tau) { m = t + 1; break; }
-        }
-        if (p.k_cap > 0) m = min(m, p.k_cap);
-        kept_prefix = m;
-      }
-    }
-    __syncthreads();
-    const int m = kept_prefix;
+      for (int s = 0; s < D / 4; ++s) b[s] = kt[(size_t)(4 * s + kl) * Nb + cc];
+      f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = e * kThreads + tid;
-      if (i < m) {
-        const int c = key_block(kv[e]);
-        atomicOr(&word[c >> 5], 1u << (c & 31));
+      for (int s = 0; s < D / 4; s += 2) {
+        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], b[s + 1], acc1, 0, 0, 0);
       }
-    }
-    for (int c = tid; c < Nb; c += kThreads) {
-      const bool forced = (p.keep_diag && c == r) || (c < p.n_text_blocks) ||
-                          static_keep(pid, prm, r, c, g.N, g.blk, Nb);
-      if (forced) atomicOr(&word[c >> 5], 1u << (c & 31));
+      if (c < Nb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) srow[4 * e + kl][c] = (acc0[e] + acc1[e]) / sqrt_d;
+      }
     }
   }
   __syncthreads();
-  if (tid < g.words) bits[(size_t)row * g.words + tid] = word[tid];
-  if (tid < 64) {
-    int pc = tid < g.words ? __popc(word[tid]) : 0;
-    for (int off = 32; off > 0; off >>= 1) pc += __shfl_xor(pc, off, 64);
-    if (tid == 0) count[row] = pc;
+
+  // Marks the kept blocks of tile row rr (block row r): slots for which kept(e) holds, plus
+  // the forced and static blocks; a query block holding text tokens keeps every block.
+  auto mark_row = [&](int rr, int r, const uint64_t (&kv)[PER], auto kept) {
+    if (r >= Nb) return;
+    if (r < p.n_text_blocks) {
+      for (int c = lane; c < Nb; c += 64) atomicOr(&word[rr][c >> 5], 1u << (c & 31));
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (kept(e)) {
+        const int c = key_block(kv[e]);
+        atomicOr(&word[rr][c >> 5], 1u << (c & 31));
+      }
+    }
+    for (int c = lane; c < Nb; c += 64) {
+      const bool forced = (p.keep_diag && c == r) || (c < p.n_text_blocks) ||
+                          static_keep(pid, prm, r, c, g.N, g.blk, Nb);
+      if (forced) atomicOr(&word[rr][c >> 5], 1u << (c & 31));
+    }
+  };
+
+  if (p.mode == 0) {
+    // Top-k ranks by the score itself: exp is increasing, so the order by P equals the
+    // order by S wherever the S values differ by more than float64 rounding of P can hide
+    // (a top-k boundary closer than that is a near-tie, see ambiguous rows).  The kept set
+    // is every key at or above the m-th largest, found without sorting.
+    const int m = min(max(p.k, 0), Nb);
+    for (int t = 0; t < kRankRowsPerWave; ++t) {
+      const int rr = w * kRankRowsPerWave + t;
+      uint64_t kv[PER], real[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int c = lane * PER + e;
+        kv[e] = c < Nb ? rank_key(srow[rr][c], c) : 0ull;
+        real[e] = __ballot(c < Nb);
+      }
+      const uint64_t thr = m > 0 && m < Nb ? select_kth<PER>(kv, real, m) : 0ull;
+      mark_row(rr, r0 + rr, kv, [&](int e) { return m > 0 && lane * PER + e < Nb && kv[e] >= thr; });
+    }
+  } else {
+    // The mass prefix needs P itself (softmax over all key blocks of the row, whose
+    // numerators replace the scores in LDS) and the rank order up to its end: the rows are
+    // sorted, RI at a time.
+    for (int pass = 0; pass < kRankRowsPerWave / RI; ++pass) {
+      const int rr0 = w * kRankRowsPerWave + pass * RI;   // first tile row of this pass
+      uint64_t kv[RI][PER];
+      double z[RI];
+#pragma unroll
+      for (int j = 0; j < RI; ++j) {
+        double* sr = srow[rr0 + j];
+        double mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int c = lane * PER + e;
+          if (c < Nb) mx = fmax(mx, sr[c]);
+        }
+        mx = wave_max(mx);
+        double ex[PER], part = 0.0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int c = lane * PER + e;
+          ex[e] = c < Nb ? exp(sr[c] - mx) : 0.0;
+          part += ex[e];
+          if (c < Nb) sr[c] = ex[e];
+        }
+        z[j] = wave_sum(part);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int c = lane * PER + e;
+          kv[j][e] = c < Nb ? rank_key(ex[e] / z[j], c) : 0ull;
+        }
+      }
+      rank_sort_desc<PER, RI, NP2, 2>(kv, lane);
+      __syncthreads();   // numerators visible to every lane
+#pragma unroll
+      for (int j = 0; j < RI; ++j) {
+        const int rr = rr0 + j;
+        // running mass in rank order: a sequential sum over each lane's slots, then a
+        // wavefront scan of the lane totals; the first rank reaching tau ends the prefix
+        double cum[PER], run = 0.0;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int i = lane * PER + e;
+          run += i < Nb ? srow[rr][key_block(kv[j][e])] / z[j] : 0.0;
+          cum[e] = run;
+        }
+        double incl = run;
+        for (int off = 1; off < 64; off <<= 1) {
+          const double u = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += u;
+        }
+        double excl = __shfl_up(incl, 1, 64);
+        if (lane == 0) excl = 0.0;
+        int first = 0x7fffffff;
+#pragma unroll
+        for (int e = PER - 1; e >= 0; --e) {
+          const int i = lane * PER + e;
+          if (i < Nb && excl + cum[e] >= p.tau) first = i;
+        }
+        first = wave_min_int(first);
+        int m = first == 0x7fffffff ? Nb : first + 1;
+        if (p.k_cap > 0) m = min(m, p.k_cap);
+        mark_row(rr, r0 + rr, kv[j], [&](int e) { return lane * PER + e < m; });
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < nrows * g.words; i += kRankThreads) bits[row0 * g.words + i] = word[i / g.words][i % g.words];
+  if (tid < nrows) {
+    int pc = 0;
+    for (int x = 0; x < g.words; ++x) pc += __popc(word[tid][x]);
+    count[row0 + tid] = pc;
   }
 }
 
@@ -584,7 +652,6 @@ size_t mask_workspace_layout(const MaskGeom& g, bool adaptive, MaskWorkspace* ws
   if (adaptive) {
     w.qp = static_cast<double*>(take(rows * g.d * sizeof(double)));
     w.kpt = static_cast<double*>(take(rows * g.d * sizeof(double)));
-    w.score = static_cast<double*>(take(rows * g.Nb * sizeof(double)));
   }
   w.bits = static_cast<uint32_t*>(take(rows * g.words * sizeof(uint32_t)));
   w.count = static_cast<int32_t*>(take(rows * sizeof(int32_t)));
@@ -609,21 +676,26 @@ hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& 
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const MaskGeom& g, const MaskWorkspace& ws, hipStream_t s) {
-  const int tiles = (g.Nb + kST - 1) / kST;
-  const dim3 grid((unsigned)(g.B * g.H * tiles * tiles));
-  if (g.d == 128)
-    hipLaunchKernelGGL(score_kernel<128>, grid, dim3(kThreads), 0, s, ws.qp, ws.kpt, ws.score, g.Nb);
-  else
-    hipLaunchKernelGGL(score_kernel<64>, grid, dim3(kThreads), 0, s, ws.qp, ws.kpt, ws.score, g.Nb);
+template <int D>
+static hipError_t launch_rank_d(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
+                                const MaskWorkspace& ws, hipStream_t s) {
+  const int tiles = (g.Nb + kRankRows - 1) / kRankRows;
+  const dim3 grid((unsigned)(g.B * g.H * tiles)), block(kRankThreads);
+  int np2 = 64;
+  while (np2 < g.Nb) np2 <<= 1;
+  switch (np2) {
+    case 64: hipLaunchKernelGGL((rank_kernel<D, 64>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
+    case 128: hipLaunchKernelGGL((rank_kernel<D, 128>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
+    case 256: hipLaunchKernelGGL((rank_kernel<D, 256>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
+    case 512: hipLaunchKernelGGL((rank_kernel<D, 512>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
+    default: hipLaunchKernelGGL((rank_kernel<D, 1024>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_select(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
-                         const MaskWorkspace& ws, hipStream_t s) {
-  const dim3 grid((unsigned)(g.B * g.H * g.Nb));
-  hipLaunchKernelGGL(select_kernel, grid, dim3(kThreads), 0, s, ws.score, ws.bits, ws.count, g, p, heads);
-  return hipGetLastError();
+hipError_t launch_rank(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
+                       const MaskWorkspace& ws, hipStream_t s) {
+  return g.d == 128 ? launch_rank_d<128>(g, p, heads, ws, s) : launch_rank_d<64>(g, p, heads, ws, s);
 }
 
 hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const MaskWorkspace& ws,

@@ -135,8 +135,7 @@ const char* asa_last_error(void);
  * the kept count is known only on the device).  Returns -1 for an invalid shape. */
 int64_t asa_csr_capacity(const asa_shape* shape);
 
-/* Workspace bytes for asa_build_mask (pooled Q and K, block scores, row bitmasks and
- * counts).  Returns 0 for an invalid shape. */
+/* Workspace bytes for asa_build_mask (pooled Q and K, row bitmasks and counts).  Returns 0 for an invalid shape. */
 size_t asa_build_mask_workspace_size(const asa_shape* shape);
 
 /* Workspace bytes for asa_static_mask (row bitmasks and counts).  0 for an invalid shape. */

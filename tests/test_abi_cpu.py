@@ -62,7 +62,7 @@ def test_capacity_and_workspace_sizes():
     assert asa.lib.asa_csr_capacity(ctypes.byref(s)) == 2 * 16 * 16
     ws = asa.lib.asa_build_mask_workspace_size(ctypes.byref(s))
     rows = 2 * 16
-    assert ws >= rows * 64 * 8 * 2 + rows * 16 * 8 + rows * 4 + rows * 4
+    assert ws >= rows * 64 * 8 * 2 + rows * 4 + rows * 4   # pooled Q and K (float64), bitmasks, counts
     assert asa.lib.asa_static_mask_workspace_size(ctypes.byref(s)) >= rows * 8
     assert asa.lib.asa_build_mask_workspace_size(ctypes.byref(_shape(d=96))) == 0
     assert asa.lib.asa_csr_capacity(None) == -1
