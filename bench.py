@@ -269,7 +269,7 @@ def main():
 
         def backward():
             asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], out, gout, lse, row_ptr, col_idx, blk,
-                                  grads=grads, workspace=bws)
+                                  order=order, grads=grads, workspace=bws)
 
         for _ in range(3):
             backward()

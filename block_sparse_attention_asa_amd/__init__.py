@@ -340,10 +340,12 @@ def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
                       dout: torch.Tensor, lse: torch.Tensor, row_ptr: torch.Tensor,
                       col_idx: torch.Tensor, blk: int, *,
                       patterns: Optional[Sequence[Tuple[int, int]]] = None, scale: float = 0.0,
+                      order: Optional[torch.Tensor] = None,
                       grads: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None):
     """Gradients (dQ, dK, dV), float32 [B,H,N,d], of sum(dout * O) for the block-sparse
-    attention O = asa_attention_fwd(q, k, v, row_ptr, col_idx, blk) with its `lse`."""
+    attention O = asa_attention_fwd(q, k, v, row_ptr, col_idx, blk) with its `lse`.
+    `order` (a mask builder's schedule) sets the dQ pass's row order, as for the forward."""
     _require_device(q, k, v, o, dout, lse, row_ptr, col_idx)
     if not (q.shape == k.shape == v.shape == o.shape == dout.shape):
         raise ValueError("q, k, v, o and dout must share one shape")
@@ -357,6 +359,10 @@ def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
         raise TypeError("row_ptr and col_idx must be int32")
     if row_ptr.numel() != B * H * num_blocks(N, blk) + 1:
         raise ValueError("row_ptr length does not match [B, H, Nb] rows")
+    if order is not None:
+        _require_device(order)
+        if order.dtype != torch.int32 or order.numel() != row_ptr.numel() - 1:
+            raise ValueError("order must be int32 with one entry per CSR row")
     if grads is None:
         grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) for _ in range(3))
     dq, dk, dv = grads
@@ -367,7 +373,7 @@ def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     need = int(lib.asa_attention_bwd_workspace_size(ctypes.byref(shp)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    csr = _csr_struct(row_ptr, col_idx, None)
+    csr = _csr_struct(row_ptr, col_idx, order)
     pats = _patterns(patterns, H)
     _check(lib.asa_attention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _dtype_code(o),
                                  dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),

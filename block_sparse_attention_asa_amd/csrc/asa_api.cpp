@@ -425,6 +425,7 @@ asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const 
   a.dq = dQ; a.dk = dK; a.dv = dV;
   a.row_ptr = csr->row_ptr;
   a.col_idx = csr->col_idx;
+  a.order = csr->order;
   a.o_bf16 = o_dtype == ASA_BF16;
   const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)shape->d);
   a.scale = (float)sc;

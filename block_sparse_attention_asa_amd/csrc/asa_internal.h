@@ -21,6 +21,11 @@ __host__ __device__ inline void xcd_range(int x, int total, int& lo, int& hi) {
   hi = lo + per + (x < rem ? 1 : 0);
 }
 
+// Skipped heads as a bitmask, passed by value.
+struct SkipBits {
+  uint32_t bits[kMaxHeads / 32];
+};
+
 // Per-head pattern table passed by value (2 KiB of kernel arguments).
 struct HeadTable {
   int32_t id[kMaxHeads];
@@ -99,6 +104,8 @@ struct BwdArgs {
   const int32_t* col_idx;
   int32_t* col_ptr;        // transposed mask (workspace): [B*H*Nb + 1]
   int32_t* row_idx;        // [B*H*Nb*Nb] capacity, query blocks ascending per key block
+  int32_t* col_order;      // [B*H*Nb] key-block processing order (workspace)
+  const int32_t* order;    // [B*H*Nb] row processing order from the CSR, or NULL
   float* ld;               // [B*H*N][2] (lse * log2(e), D = dO . O) per query (workspace)
   int32_t B, H, N, d, blk, Nb;
   bool o_bf16;

@@ -15,7 +15,9 @@
 //   bwd_prep_kernel  per query: (lse * log2 e, D = dO . O) -> workspace pairs.
 //   csc_kernel       one workgroup per head: CSR -> CSC (key block -> query blocks in
 //                    ascending order) through a transposed bitmask in LDS.
-//   dq_kernel        one workgroup per query-block row, like the forward: K and V of every
+//   col_order_kernel the key-block schedule: longest lists first inside each XCD range.
+//   dq_kernel        one workgroup per query-block row, like the forward (and in the CSR's
+//                    processing order when there is one): K and V of every
 //                    kept key block stream through an LDS ring; per 64-key step
 //                    S^T = K Q^T, P^T = exp2(S^T s - lse), dP^T = V dO^T,
 //                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T  (K^T by transpose reads).
@@ -29,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include "attn_common.h"
+#include "order.h"
 
 namespace asa {
 namespace {
@@ -138,6 +141,22 @@ __global__ __launch_bounds__(kCscThreads) void csc_kernel(const int32_t* __restr
   if (bh == heads - 1 && tid == 0) col_ptr[heads * Nb] = row_ptr[heads * Nb];
 }
 
+// Key-block schedule for dkv_kernel: inside each XCD range, key blocks by descending length
+// class of their query-block lists (skipped heads count as empty), so the blocks kept by
+// many query blocks start first.  One workgroup per XCD range.
+__global__ __launch_bounds__(kOrderThreads) void col_order_kernel(const int32_t* __restrict__ col_ptr,
+                                                                  int32_t* __restrict__ col_order,
+                                                                  int Nb, int H, int total,
+                                                                  SkipBits skip) {
+  __shared__ OrderScratch sh;
+  order_range(
+      [&](int i) {
+        const int h = (i / Nb) % H;
+        return ((skip.bits[h >> 5] >> (h & 31)) & 1u) ? 0 : col_ptr[i + 1] - col_ptr[i];
+      },
+      col_order, total, blockIdx.x, sh);
+}
+
 // V^T-style fragment by transpose reads: rows kbase.. of a row-major swizzled [rows][D]
 // bf16 tile, columns 32*io + ..; element j of lane half hf comes from row
 // 16*u + 8*(j/4) + 4*hf + j%4 (the k order of the MFMA output layout).  Lane s of 16-lane
@@ -210,7 +229,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   const int N = a.N, Nb = a.Nb, H = a.H;
   const int total_rows = a.B * H * Nb;
-  const int row = xcd_row(blockIdx.x, total_rows);
+  const int pos = xcd_row(blockIdx.x, total_rows);
+  const int row = a.order ? __builtin_amdgcn_readfirstlane(a.order[pos]) : pos;
   const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qn = lane & 31, hf = lane >> 5;
@@ -377,7 +397,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   const int N = a.N, Nb = a.Nb, H = a.H;
   const int total = a.B * H * Nb;
-  const int col = xcd_row(blockIdx.x, total);
+  const int col = __builtin_amdgcn_readfirstlane(a.col_order[xcd_row(blockIdx.x, total)]);
   const int bh = col / Nb, c = col - bh * Nb, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qn = lane & 31, hf = lane >> 5;
@@ -551,10 +571,12 @@ size_t bwd_workspace_layout(const BwdArgs& g, BwdArgs* a, void* base) {
   float* ld = static_cast<float*>(take((2 * nq + 64) * sizeof(float)));
   int32_t* col_ptr = static_cast<int32_t*>(take((rows + 1) * sizeof(int32_t)));
   int32_t* row_idx = static_cast<int32_t*>(take(rows * g.Nb * sizeof(int32_t)));
+  int32_t* col_order = static_cast<int32_t*>(take(rows * sizeof(int32_t)));
   if (a) {
     a->ld = ld;
     a->col_ptr = col_ptr;
     a->row_idx = row_idx;
+    a->col_order = col_order;
   }
   return off;
 }
@@ -582,6 +604,12 @@ hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(csc_kernel, dim3((unsigned)(a.B * a.H)), dim3(kCscThreads), 0, s, a.row_ptr, a.col_idx,
                      a.col_ptr, a.row_idx, a.Nb, a.B * a.H);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SkipBits sk;
+  for (int i = 0; i < kMaxHeads / 32; ++i) sk.bits[i] = a.skip_bits[i];
+  hipLaunchKernelGGL(col_order_kernel, dim3(kXcds), dim3(kOrderThreads), 0, s, a.col_ptr, a.col_order, a.Nb,
+                     a.H, a.B * a.H * a.Nb, sk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.d == 128 && a.blk == 128) return launch_grads<128, 128>(a, s);

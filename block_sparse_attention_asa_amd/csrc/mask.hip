@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include "asa_internal.h"
+#include "order.h"
 
 namespace asa {
 namespace {
@@ -487,84 +488,7 @@ __global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__
 }
 
 // ------------------------------------------------------------------ CSR
-constexpr int kScanThreads = 1024;
-
-// Processing order for the attention kernel: inside each XCD's contiguous row range, rows
-// by descending length class, stable in row index, so long rows (text rows, full heads)
-// start first and do not form the tail.  Class of a row with c kept blocks: 0 for c = 0,
-// else 1 + floor(log2 c).  One workgroup of the scan launch per range, beside the one that
-// scans: every thread owns a run of consecutive rows and counts them per class, a
-// workgroup scan per class gives each thread its output slots, and the rows are written
-// in order (deterministic).
-constexpr int kOrderClasses = 12;   // c <= kMaxMaskBlocks = 2^10 -> classes 0..11
-
-__device__ inline int length_class(int c) { return c <= 0 ? 0 : 32 - __clz(c); }
-
-struct OrderScratch {
-  int wsum[kScanThreads / 64][kOrderClasses];
-  int base[kOrderClasses];
-};
-
-__device__ void order_range(const int32_t* __restrict__ count, int32_t* __restrict__ order, int rows,
-                            int x, OrderScratch& sh) {
-  int lo, hi;
-  xcd_range(x, rows, lo, hi);
-  const int n = hi - lo;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int t0 = lo + threadIdx.x * per, t1 = min(t0 + per, hi);
-  int cnt[kOrderClasses];
-#pragma unroll
-  for (int k = 0; k < kOrderClasses; ++k) cnt[k] = 0;
-  for (int i = t0; i < t1; ++i) {
-    const int cl = length_class(count[i]);
-#pragma unroll
-    for (int k = 0; k < kOrderClasses; ++k) cnt[k] += cl == k ? 1 : 0;
-  }
-  // inclusive scan of each class count over the threads of a wavefront, then over waves
-  int incl[kOrderClasses];
-#pragma unroll
-  for (int k = 0; k < kOrderClasses; ++k) {
-    int v = cnt[k];
-    for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(v, off, 64);
-      if (lane >= off) v += u;
-    }
-    incl[k] = v;
-    if (lane == 63) sh.wsum[wv][k] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < kOrderClasses) {   // exclusive wave offsets and class totals
-    const int k = threadIdx.x;
-    int run = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-      const int v = sh.wsum[w][k];
-      sh.wsum[w][k] = run;
-      run += v;
-    }
-    sh.base[k] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {   // class starts, longest class first
-    int start = 0;
-    for (int k = kOrderClasses - 1; k >= 0; --k) {
-      const int tot = sh.base[k];
-      sh.base[k] = start;
-      start += tot;
-    }
-  }
-  __syncthreads();
-  int slot[kOrderClasses];
-#pragma unroll
-  for (int k = 0; k < kOrderClasses; ++k) slot[k] = lo + sh.base[k] + sh.wsum[wv][k] + incl[k] - cnt[k];
-  for (int i = t0; i < t1; ++i) {
-    const int cl = length_class(count[i]);
-#pragma unroll
-    for (int k = 0; k < kOrderClasses; ++k) {
-      if (cl == k) order[slot[k]++] = i;
-    }
-  }
-}
+constexpr int kScanThreads = kOrderThreads;   // the scan launch also builds the order
 
 // Workgroup 0: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].  Each thread owns a
 // run of consecutive rows; one wave-level scan of the per-thread totals.
@@ -575,7 +499,7 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* _
   __shared__ int wsum[kScanThreads / 64];
   __shared__ OrderScratch osh;
   if (blockIdx.x > 0) {   // workgroups 1..8: the processing order of one XCD range each
-    order_range(count, order, rows, blockIdx.x - 1, osh);
+    order_range([&](int i) { return count[i]; }, order, rows, blockIdx.x - 1, osh);
     return;
   }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

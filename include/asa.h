@@ -256,8 +256,9 @@ asa_status asa_attention_fwd_split(const void* Q, const void* K, const void* V, 
                                    int32_t split_blocks, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
-/* Workspace bytes for asa_attention_bwd: the per-query (lse, D) pairs and the transposed
- * mask (key block -> query blocks), sized for the worst case B*H*Nb*Nb kept tiles.
+/* Workspace bytes for asa_attention_bwd: the per-query (lse, D) pairs, the transposed
+ * mask (key block -> query blocks), sized for the worst case B*H*Nb*Nb kept tiles, and the
+ * key-block processing order.
  * Returns 0 for an invalid shape (including Nb > 1024). */
 size_t asa_attention_bwd_workspace_size(const asa_shape* shape);
 
@@ -279,7 +280,10 @@ size_t asa_attention_bwd_workspace_size(const asa_shape* shape);
  * lse          device float32 [B,H,N] from asa_attention_fwd_lse for the same inputs.
  * dQ, dK, dV   device float32 [B,H,N,d], fully written (zero where no kept tile
  *              contributes, and for ASA_PAT_SKIP heads).
- * csr          the mask the forward used (col_idx entries in [0, Nb), unique per row).
+ * csr          the mask the forward used (col_idx entries in [0, Nb), unique per row).  A
+ *              non-NULL csr->order is the dQ pass's row schedule, as for the forward; the
+ *              dK/dV pass schedules key blocks by the same rule (longest lists first inside
+ *              each XCD range).  The gradients are bit-identical either way.
  * patterns     host array [H] or NULL; ASA_PAT_SKIP heads get zero gradients.
  * scale        the forward's scale; <= 0 selects 1/sqrt(d).
  * workspace    device buffer of at least asa_attention_bwd_workspace_size(shape) bytes,

@@ -145,6 +145,28 @@ def test_backward_deterministic(asa_lib):
         assert torch.equal(u, w)
 
 
+def test_backward_schedules_change_nothing(asa_lib):
+    """The dQ pass in the mask builder's row order, and the dK/dV pass in its own key-block
+    order, give the same bits as row order: every gradient element is summed by one lane in
+    a fixed order whatever the schedule."""
+    asa = asa_lib
+    cfg = gen.scaled(gen.COGVIDEOX, H=3, frames=2)   # text rows and popular key blocks: uneven lists
+    x = gen.make_inputs(cfg)
+    xd = to_device(x)
+    rp, ci, order = asa.asa_build_mask(xd["q"], xd["k"], cfg.blk, cfg.mode, k_top=cfg.k, tau=cfg.tau,
+                                       k_cap=cfg.k_cap, n_text=cfg.n_text, keep_diag=cfg.keep_diag,
+                                       with_order=True)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
+    o = asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp, ci, cfg.blk, order=order, lse=lse)
+    dout = _dout(tuple(x["q"].shape), 6).to("cuda:0")
+    a = asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], o, dout, lse, rp, ci, cfg.blk)
+    b = asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], o, dout, lse, rp, ci, cfg.blk, order=order)
+    torch.cuda.synchronize()
+    say(f"case {cfg.name}: backward with and without the row schedule")
+    for name, u, w in zip(("dQ", "dK", "dV"), a, b):
+        assert torch.equal(u, w), name
+
+
 def test_backward_full_size_sampled(asa_lib):
     """Wan-shaped layer at full size (B=1, H=12, N=32760, d=128, top-26): the GPU computes all
     of dQ, dK, dV; the oracle checks sampled query blocks (dQ) and sampled key blocks (dK, dV:
