@@ -299,6 +299,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __rest
   static_assert(kRankRowsPerWave % RI == 0, "rows per wavefront split into equal passes");
   __shared__ double srow[kRankRows][NP2];
   __shared__ uint32_t word[kRankRows][kMaxMaskBlocks / 32];
+  __shared__ double qtile[kRankRows][D + 1];   // the rows' pooled queries (padded rows)
 
   const int Nb = g.Nb;
   const int tiles = (Nb + kRankRows - 1) / kRankRows;
@@ -321,12 +322,21 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __rest
   {  // scores of the tile's rows
     // Rows past Nb and columns past Nb read clamped (valid) addresses: they only feed
     // outputs that are never used, and unconditional loads can all be in flight at once.
+    // the 16 rows' pooled queries (contiguous in Qp) go through LDS once, in 16-byte loads;
+    // the A fragments are then read from there
     const double* q = qp + (size_t)bh * Nb * D;
     const double* kt = kpt + (size_t)bh * D * Nb;
-    const int ra = min(r0 + (lane & 15), Nb - 1), kl = lane >> 4;
+    for (int i = tid; i < kRankRows * (D / 2); i += kRankThreads) {
+      const int rr = i / (D / 2), c2 = i - rr * (D / 2);
+      const double2 v = reinterpret_cast<const double2*>(q + (size_t)min(r0 + rr, Nb - 1) * D)[c2];
+      qtile[rr][2 * c2] = v.x;
+      qtile[rr][2 * c2 + 1] = v.y;
+    }
+    __syncthreads();
+    const int kl = lane >> 4;
     double a[D / 4], b[D / 4];
 #pragma unroll
-    for (int s = 0; s < D / 4; ++s) a[s] = q[(size_t)ra * D + 4 * s + kl];
+    for (int s = 0; s < D / 4; ++s) a[s] = qtile[lane & 15][4 * s + kl];
     const double sqrt_d = sqrt((double)D);
     const int ctiles = (Nb + 15) / 16;
     for (int ct = w; ct < ctiles; ct += kRankWaves) {
