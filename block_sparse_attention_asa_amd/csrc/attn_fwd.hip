@@ -30,7 +30,9 @@ namespace {
 
 // Each kept key block is consumed in steps of KT keys.  K and V of a step share one slot of
 // a two-slot LDS ring: while the workgroup computes on one slot, the next step's K and V
-// stream into the other, so a step needs a single barrier.
+// stream into the other, so a step needs a single barrier.  The step loop is unrolled by
+// two so that each copy works on a fixed slot (fixed LDS addresses, no per-step address
+// arithmetic).
 // kSplit: the launch cuts long rows into chunks (meta.split_blocks > 0); a separate
 // instantiation keeps the registers of the plain kernel untouched.
 template <typename T, typename TO, int D, int BLK, bool kSplit>
@@ -145,154 +147,160 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
     int e = e0, hh = 0;
     int c = __builtin_amdgcn_readlane(cvec, 0);
     int nkv = min(BLK, N - c * BLK);
-    int slot = 0;
     {
       const size_t src = head + (size_t)c * BLK * D;
       dma_step(K + src, V + src, 0, min(KT, nkv));
     }
 
-    for (;;) {
-      // the step after this one (skips steps holding no valid key)
-      int e_n = e, hh_n = hh + 1, c_n = c, nkv_n = nkv;
-      if (hh_n >= kSteps || hh_n * KT >= nkv) {
-        e_n = e + 1;
-        hh_n = 0;
-        if (e_n < e1) {
-          if (e_n - cbase == 64) {   // next batch of indices (rows longer than 64 blocks)
-            cbase += 64;
-            cvec = cbase + lane < e1 ? col_idx[cbase + lane] : 0;
+    // One step on ring slot kSlot (a compile-time constant, so the LDS addresses of both
+    // slots are fixed and the slot offset is an immediate); returns whether a step follows.
+    auto step = [&](auto slot_c) -> bool {
+      constexpr int kSlot = decltype(slot_c)::value;
+        // the step after this one (skips steps holding no valid key)
+        int e_n = e, hh_n = hh + 1, c_n = c, nkv_n = nkv;
+        if (hh_n >= kSteps || hh_n * KT >= nkv) {
+          e_n = e + 1;
+          hh_n = 0;
+          if (e_n < e1) {
+            if (e_n - cbase == 64) {   // next batch of indices (rows longer than 64 blocks)
+              cbase += 64;
+              cvec = cbase + lane < e1 ? col_idx[cbase + lane] : 0;
+            }
+            c_n = __builtin_amdgcn_readlane(cvec, e_n - cbase);
+            nkv_n = min(BLK, N - c_n * BLK);
           }
-          c_n = __builtin_amdgcn_readlane(cvec, e_n - cbase);
-          nkv_n = min(BLK, N - c_n * BLK);
         }
-      }
-      const bool more = e_n < e1;
-      const int nv = min(KT, nkv - hh * KT);   // valid keys in this step (>= 1)
+        const bool more = e_n < e1;
+        const int nv = min(KT, nkv - hh * KT);   // valid keys in this step (>= 1)
 
-      // this step's K and V landed everywhere; every wave is done with the other slot
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      wg_barrier();
-      if (more) {
-        const size_t src = head + ((size_t)c_n * BLK + hh_n * KT) * D;
-        dma_step(K + src, V + src, slot ^ 1, min(KT, nkv_n - hh_n * KT));
-      }
-      const uint4* kt = Kt[slot];
-      const T* vt = reinterpret_cast<const T*>(Vt[slot]);
+        // this step's K and V landed everywhere; every wave is done with the other slot
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        wg_barrier();
+        if (more) {
+          const size_t src = head + ((size_t)c_n * BLK + hh_n * KT) * D;
+          dma_step(K + src, V + src, kSlot ^ 1, min(KT, nkv_n - hh_n * KT));
+        }
+        const uint4* kt = Kt[kSlot];
+        const T* vt = reinterpret_cast<const T*>(Vt[kSlot]);
 
-      // S^T = K Q^T
-      f32x16_t s[kSub];
-#pragma unroll
-      for (int is = 0; is < kSub; ++is) {
-        s[is] = f32x16_t{};
-        const int kr = 32 * is + qn;
-#pragma unroll
-        for (int t = 0; t < kQk; ++t) {
-          Frag<T> a;
-          if constexpr (kBf16) {
-            a.v = kt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
-          } else {
-            a.a = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf) ^ swz<GPR>(kr))]);
-            a.b = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz<GPR>(kr))]);
+        // S^T = K Q^T
+        f32x16_t s[kSub];
+  #pragma unroll
+        for (int is = 0; is < kSub; ++is) {
+          s[is] = f32x16_t{};
+          const int kr = 32 * is + qn;
+  #pragma unroll
+          for (int t = 0; t < kQk; ++t) {
+            Frag<T> a;
+            if constexpr (kBf16) {
+              a.v = kt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
+            } else {
+              a.a = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf) ^ swz<GPR>(kr))]);
+              a.b = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz<GPR>(kr))]);
+            }
+            mma_k16(s[is], a, qf[t]);
           }
-          mma_k16(s[is], a, qf[t]);
         }
-      }
-      // keys past N exist only in the last, partial key block
-      if (nv < KT) {
-#pragma unroll
+        // keys past N exist only in the last, partial key block
+        if (nv < KT) {
+  #pragma unroll
+          for (int is = 0; is < kSub; ++is)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (32 * is + 8 * (i >> 2) + 4 * hf + (i & 3) >= nv) s[is][i] = -INFINITY;
+        }
+        // row max of the raw scores (scale > 0 commutes with max), both lane halves
+        float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
+  #pragma unroll
         for (int is = 0; is < kSub; ++is)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (32 * is + 8 * (i >> 2) + 4 * hf + (i & 3) >= nv) s[is][i] = -INFINITY;
-      }
-      // row max of the raw scores (scale > 0 commutes with max), both lane halves
-      float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
-#pragma unroll
-      for (int is = 0; is < kSub; ++is)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mc[(i >> 1) & 3] = max3(mc[(i >> 1) & 3], s[is][i], s[is][i + 1]);
-      float mx = max3(mc[0], mc[1], max3(mc[2], mc[3], mc[3]));
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = max3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
-      }
-      const float m_tile = mx * scale_log2;
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
-        const float m_new = __builtin_fmaxf(m_run, m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
-      }
-      const float neg_m = -m_run;
-      Frag<T> pf[kPv];
-#pragma unroll
-      for (int u = 0; u < kPv; ++u) {
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_m));
-        if constexpr (kBf16) {
-          uint32_t wd[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2_t pk = {static_cast<__bf16>(pv[2 * j]), static_cast<__bf16>(pv[2 * j + 1])};
-            wd[j] = __builtin_bit_cast(uint32_t, pk);
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
-          }
-          pf[u].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) l_run += pv[j];
-          pf[u].a = make_float4(pv[0], pv[1], pv[2], pv[3]);
-          pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
+  #pragma unroll
+          for (int i = 0; i < 16; i += 2) mc[(i >> 1) & 3] = max3(mc[(i >> 1) & 3], s[is][i], s[is][i + 1]);
+        float mx = max3(mc[0], mc[1], max3(mc[2], mc[3], mc[3]));
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = max3(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
         }
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int io = 0; io < kOut; ++io) {
-#pragma unroll
+        const float m_tile = mx * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleSlack) != 0) {
+          const float m_new = __builtin_fmaxf(m_run, m_tile);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+  #pragma unroll
+          for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
+        }
+        const float neg_m = -m_run;
+        Frag<T> pf[kPv];
+  #pragma unroll
         for (int u = 0; u < kPv; ++u) {
-          Frag<T> a;
+          float pv[8];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j)
+            pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_m));
           if constexpr (kBf16) {
-            // transpose reads: lane s of 16-lane group g supplies row kbase + s/4, columns
-            // dbase + 4*(s%4) .. +3; lane i of the group receives column dbase + i of rows
-            // kbase .. kbase+3, i.e. V^T[d][4 consecutive keys].
-            const int g = lane >> 4, sl = lane & 15;
-            const int dcol = 32 * io + 16 * (g & 1) + 4 * (sl & 3);
-            short4_t part[2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-              const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
-              const int gran = (dcol >> 3) ^ swz<GPR>(kr);
-              const uint16_t* p = vt + kr * D + gran * 8 + (dcol & 7);
-              part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) short4_t*)(p));
+            uint32_t wd[4];
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2_t pk = {static_cast<__bf16>(pv[2 * j]), static_cast<__bf16>(pv[2 * j + 1])};
+              wd[j] = __builtin_bit_cast(uint32_t, pk);
+              l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
             }
-            const uint2 lo = __builtin_bit_cast(uint2, part[0]);
-            const uint2 hi = __builtin_bit_cast(uint2, part[1]);
-            a.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            pf[u].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
           } else {
-            const int d = 32 * io + qn;
-            float av[8];
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-              const int kr = 16 * u + 8 * (jj >> 2) + 4 * hf + (jj & 3);
-              av[jj] = vt[(kr * GPR + ((d / G) ^ swz<GPR>(kr))) * G + (d % G)];
-            }
-            a.a = make_float4(av[0], av[1], av[2], av[3]);
-            a.b = make_float4(av[4], av[5], av[6], av[7]);
+  #pragma unroll
+            for (int j = 0; j < 8; ++j) l_run += pv[j];
+            pf[u].a = make_float4(pv[0], pv[1], pv[2], pv[3]);
+            pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
           }
-          mma_k16(acc[io], a, pf[u]);
         }
-      }
-      if (!more) break;
+        // O^T += V^T P^T
+  #pragma unroll
+        for (int io = 0; io < kOut; ++io) {
+  #pragma unroll
+          for (int u = 0; u < kPv; ++u) {
+            Frag<T> a;
+            if constexpr (kBf16) {
+              // transpose reads: lane s of 16-lane group g supplies row kbase + s/4, columns
+              // dbase + 4*(s%4) .. +3; lane i of the group receives column dbase + i of rows
+              // kbase .. kbase+3, i.e. V^T[d][4 consecutive keys].
+              const int g = lane >> 4, sl = lane & 15;
+              const int dcol = 32 * io + 16 * (g & 1) + 4 * (sl & 3);
+              short4_t part[2];
+  #pragma unroll
+              for (int tt = 0; tt < 2; ++tt) {
+                const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
+                const int gran = (dcol >> 3) ^ swz<GPR>(kr);
+                const uint16_t* p = vt + kr * D + gran * 8 + (dcol & 7);
+                part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4_t*)(p));
+              }
+              const uint2 lo = __builtin_bit_cast(uint2, part[0]);
+              const uint2 hi = __builtin_bit_cast(uint2, part[1]);
+              a.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+              const int d = 32 * io + qn;
+              float av[8];
+  #pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const int kr = 16 * u + 8 * (jj >> 2) + 4 * hf + (jj & 3);
+                av[jj] = vt[(kr * GPR + ((d / G) ^ swz<GPR>(kr))) * G + (d % G)];
+              }
+              a.a = make_float4(av[0], av[1], av[2], av[3]);
+              a.b = make_float4(av[4], av[5], av[6], av[7]);
+            }
+            mma_k16(acc[io], a, pf[u]);
+          }
+        }
+      if (!more) return false;
       e = e_n;
       hh = hh_n;
       c = c_n;
       nkv = nkv_n;
-      slot ^= 1;
+      return true;
+    };
+    for (;;) {
+      if (!step(std::integral_constant<int, 0>{})) break;
+      if (!step(std::integral_constant<int, 1>{})) break;
     }
   }
 
