@@ -132,10 +132,11 @@ def test_dense_reference_run(asa_lib):
     compare_outputs(out.cpu().numpy(), O.dense_attention(q64, k64, v64), False, "dense")
 
 
-@pytest.mark.parametrize("N,blk,d", [(100, 128, 128), (128, 128, 64), (640, 64, 128), (1000, 64, 64),
+@pytest.mark.parametrize("N,blk,d", [(1, 64, 64), (129, 128, 128), (100, 128, 128), (128, 128, 64), (640, 64, 128), (1000, 64, 64),
                                      (4097, 128, 128)])
 def test_edge_shapes(asa_lib, N, blk, d):
-    """Single partial block, exact multiples, ragged tails; adaptive top-k, bf16 and fp32."""
+    """One token, a one-token last block, a single partial block, exact multiples, ragged
+    tails; adaptive top-k, bf16 and fp32."""
     for dtype in ("bf16", "f32"):
         cfg = gen.Config(name=f"edge_{N}_{blk}_{d}_{dtype}", seed=7, B=2, H=2, N=N, d=d, blk=blk,
                          dtype=dtype, frames=1, Hs=1, Ws=N, structure="none", mode=gen.TOPK, k=2)
