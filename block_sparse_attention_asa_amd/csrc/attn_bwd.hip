@@ -195,6 +195,15 @@ __device__ inline Frag<uint16_t> pack_bf16(const float (&x)[8]) {
   return f;
 }
 
+// Clear the bf16 elements of a packed fragment whose index is in the pair masks: word j
+// holds elements 2j (low half) and 2j+1.  keep_sign leaves the sign bit, which is what
+// multiplying the value by +0 before packing gives.
+__device__ inline void clear_bf16(Frag<uint16_t>& f, const uint32_t (&drop)[4], bool keep_sign) {
+  const uint32_t keep = keep_sign ? 0x80008000u : 0u;
+  f.v = make_uint4(f.v.x & (~drop[0] | keep), f.v.y & (~drop[1] | keep), f.v.z & (~drop[2] | keep),
+                   f.v.w & (~drop[3] | keep));
+}
+
 // Store a transposed [32 x 32*kOut] accumulator (lane = token row, registers = columns)
 // as fp32 rows of D: acc[io][4g + t] is column 32io + 8g + 4hf + t.
 template <int kOut, int D>
@@ -348,12 +357,19 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * h2 + j;
-            const int key = 32 * is + 8 * (i >> 2) + 4 * hf + (i & 3);
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -lse2));
-            if (nv < KT && key >= nv) p = 0.f;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -lse2));
             x[j] = p * (dp[i] - dd);
           }
           dsf[2 * is + h2] = pack_bf16(x);
+          if (nv < KT) {   // keys past N (the last, partial key block only): P = 0, so dS = +-0
+            uint32_t drop[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int key = 32 * is + 8 * (2 * h2 + (j >> 1)) + 4 * hf + 2 * (j & 1);   // element 2j
+              drop[j] = (key >= nv ? 0x0000FFFFu : 0u) | (key + 1 >= nv ? 0xFFFF0000u : 0u);
+            }
+            clear_bf16(dsf[2 * is + h2], drop, true);
+          }
         }
       }
       // dQ^T += K^T dS^T (K^T fragments by transpose reads of the K tile)
@@ -509,14 +525,23 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int i = 8 * u + 4 * j4 + t;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -ls[t]));
-            if (nq < QT && q0 + t >= nq) p = 0.f;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -ls[t]));
             pv[4 * j4 + t] = p;
             dsv[4 * j4 + t] = p * (dp[i] - ds_[t]);
           }
         }
         pf[u] = pack_bf16(pv);
         dsf[u] = pack_bf16(dsv);
+        if (nq < QT) {   // queries past N (the last, partial query block only): P = 0, dS = +-0
+          uint32_t drop[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int q = 16 * u + 8 * (j >> 1) + 4 * hf + 2 * (j & 1);   // element 2j
+            drop[j] = (q >= nq ? 0x0000FFFFu : 0u) | (q + 1 >= nq ? 0xFFFF0000u : 0u);
+          }
+          clear_bf16(pf[u], drop, false);
+          clear_bf16(dsf[u], drop, true);
+        }
       }
       // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transpose reads)
       const uint16_t* qtile = reinterpret_cast<const uint16_t*>(qt);
