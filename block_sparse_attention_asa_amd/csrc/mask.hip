@@ -149,8 +149,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 // contraction on the fp64 matrix cores (v_mfma_f64_16x16x4f64), written to LDS.  Operand
 // layout of the instruction, per lane l: A holds row l%16, k = l/16; B holds k = l/16,
 // column l%16; result component e holds row 4e + l/16, column l%16.  The A operand (the
-// rows' pooled queries) stays in registers while the wavefronts take 16-column tiles
-// in turn, with two accumulators on alternate k-steps.
+// rows' pooled queries, copied once into LDS with 16-byte loads) stays in registers while
+// the wavefronts take 16-column tiles in turn, with two accumulators on alternate k-steps.
 //
 // Selection: each of the eight wavefronts ranks kRankRowsPerWave rows.  Rank order is value
 // descending, then block index ascending, and a key packs both into one uint64: the
@@ -322,8 +322,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __rest
   {  // scores of the tile's rows
     // Rows past Nb and columns past Nb read clamped (valid) addresses: they only feed
     // outputs that are never used, and unconditional loads can all be in flight at once.
-    // the 16 rows' pooled queries (contiguous in Qp) go through LDS once, in 16-byte loads;
-    // the A fragments are then read from there
+    // The 16 rows' pooled queries are contiguous in Qp: they go through LDS once, in
+    // 16-byte loads, and the A fragments are read from there.
     const double* q = qp + (size_t)bh * Nb * D;
     const double* kt = kpt + (size_t)bh * D * Nb;
     for (int i = tid; i < kRankRows * (D / 2); i += kRankThreads) {
