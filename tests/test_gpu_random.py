@@ -1,0 +1,112 @@
+"""GPU parity on seeded random configurations: the mask builder, the forward (with lse) and,
+for bf16 inputs, the backward, against the float64 oracle.
+
+Each case draws B, H, N (ragged tails and single-block sequences included), d, blk, input
+dtype and structure, top-k or tau (with and without a cap), text tokens, the diagonal, and
+per-head static patterns (full, skip, diagonal, multi-diagonal, vertical stripe, frame
+tiles, adaptive).  The bounds are the suite's own: CSR bit-exact outside ambiguous rows;
+forward 2e-2 max / 2e-3 mean absolute (bf16 inputs), 1e-4 (fp32 inputs); lse within
+2^-8 + 1e-4; gradients within 2e-2 of the largest and 5e-3 of the mean reference entry.
+The GPU attends the oracle's own mask, so no oracle input comes from the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+from gpu_helpers import compare_masks, compare_outputs, csr_to_device, gpu_csr_rows, oracle_inputs, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+LSE_MAX_ABS = 2.0 ** -8 + 1e-4
+GRAD_MAX_REL, GRAD_MEAN_REL = 2e-2, 5e-3
+N_CASES = 32
+
+
+def _random_config(seed):
+    rng = np.random.default_rng(7000 + seed)
+    blk = int(rng.choice([64, 128]))
+    d = int(rng.choice([64, 128]))
+    Nb = int(rng.integers(1, 18))
+    N = max(1, Nb * blk - int(rng.integers(0, blk)))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+    n_text = int(rng.integers(1, min(N, 300))) if (N > 1 and rng.random() < 0.3) else 0
+    structure = str(rng.choice(["none", "lowrank", "smooth"]))
+    mode = gen.TOPK if rng.random() < 0.6 else gen.TAU
+    k = int(rng.integers(0, Nb + 3))
+    tau = float(rng.uniform(0.3, 1.0))
+    k_cap = int(rng.integers(1, Nb + 1)) if rng.random() < 0.5 else 0
+    patterns = None
+    if rng.random() < 0.5:
+        choices = [(gen.ADAPTIVE, 0), (gen.FULL, 0), (gen.SKIP, 0), (gen.DIAG, 0),
+                   (gen.MULTIDIAG, int(rng.integers(1, 4 * blk))), (gen.VSTRIPE, int(rng.integers(0, 3))),
+                   (gen.FRAME_TILE, int(rng.integers(1, max(2, N))))]
+        patterns = [choices[int(rng.integers(0, len(choices)))] for _ in range(H)]
+    cfg = gen.Config(name=f"random_{seed}", seed=9000 + seed, B=B, H=H, N=N, d=d, blk=blk,
+                     dtype="bf16" if rng.random() < 0.75 else "f32", frames=1, Hs=1, Ws=N - n_text,
+                     structure=structure, kind="adaptive", mode=mode, k=k, tau=tau, k_cap=k_cap,
+                     n_text=n_text, keep_diag=int(rng.integers(0, 2)), patterns=patterns)
+    return cfg
+
+
+def _grad_close(got, want, label):
+    g = got.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(g)), f"{label}: non-finite gradient"
+    err = np.abs(g - want)
+    smax, smean = float(np.abs(want).max()), float(np.abs(want).mean())
+    say(f"  [{label}] max abs err {err.max():.3e} (ref max {smax:.3e})  mean {err.mean():.3e} (ref mean {smean:.3e})")
+    assert err.max() <= GRAD_MAX_REL * smax + 1e-6, label
+    assert err.mean() <= GRAD_MEAN_REL * smean + 1e-7, label
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_config(asa_lib, seed):
+    asa = asa_lib
+    cfg = _random_config(seed)
+    say(f"case {cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} blk={cfg.blk} {cfg.dtype} {cfg.structure} "
+        f"mode={cfg.mode} k={cfg.k} tau={cfg.tau:.3f} cap={cfg.k_cap} text={cfg.n_text} diag={cfg.keep_diag} "
+        f"patterns={cfg.patterns}")
+    x = gen.make_inputs(cfg)
+    xd = to_device(x)
+    q64, k64, v64 = oracle_inputs(x)
+    M, det = O.build_mask(q64, k64, cfg.blk, mode=cfg.mode, k=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap,
+                          n_text=cfg.n_text, keep_diag=cfg.keep_diag, patterns=cfg.patterns,
+                          return_details=True)
+    rp_t, ci_t = asa.asa_build_mask(xd["q"], xd["k"], cfg.blk, cfg.mode, k_top=cfg.k, tau=cfg.tau,
+                                    k_cap=cfg.k_cap, n_text=cfg.n_text, keep_diag=cfg.keep_diag,
+                                    patterns=cfg.patterns)
+    torch.cuda.synchronize()
+    rp, ci = gpu_csr_rows(rp_t, ci_t)
+    amb = O.ambiguous_rows(det["S"], det["P"], mode=cfg.mode, k=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap)
+    diff = compare_masks(rp, ci, M, det, amb, cfg.mode, cfg.k, cfg.tau, cfg.k_cap)
+    say(f"  mask density {O.density(M):.4f}, ambiguous rows {int(amb.sum())}, differing rows {len(diff)}")
+
+    # forward (and lse) on the oracle's mask; skipped heads are all zeros
+    Meff = M.copy()
+    if cfg.patterns is not None:
+        for h, (pid, _) in enumerate(cfg.patterns):
+            if pid == O.SKIP:
+                Meff[:, h] = False
+    rp_o, ci_o = csr_to_device(M)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
+    out = asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp_o, ci_o, cfg.blk, patterns=cfg.patterns, lse=lse)
+    torch.cuda.synchronize()
+    compare_outputs(out.cpu().numpy(), O.attention(q64, k64, v64, Meff, cfg.blk), cfg.dtype == "f32", cfg.name)
+    L = O.attention_lse(q64, k64, Meff, cfg.blk)
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(L)
+    assert np.array_equal(np.isneginf(lg), ~fin), "lse: -inf pattern differs"
+    if fin.any():
+        assert float(np.abs(lg[fin] - L[fin]).max()) <= LSE_MAX_ABS
+
+    if cfg.dtype == "bf16" and Meff.any():
+        g = torch.from_numpy(np.random.default_rng(seed).standard_normal(tuple(x["q"].shape)).astype(np.float32))
+        dout = g.to(torch.bfloat16)
+        dq, dk, dv = asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], out, dout.to("cuda:0"), lse, rp_o, ci_o,
+                                           cfg.blk, patterns=cfg.patterns)
+        torch.cuda.synchronize()
+        rdq, rdk, rdv = O.attention_bwd(q64, k64, v64, dout.to(torch.float64).numpy(), Meff, cfg.blk)
+        _grad_close(dq, rdq, "dQ")
+        _grad_close(dk, rdk, "dK")
+        _grad_close(dv, rdv, "dV")
