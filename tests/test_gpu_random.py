@@ -1,5 +1,5 @@
-"""GPU parity on seeded random configurations: the mask builder, the forward (with lse) and,
-for bf16 inputs, the backward, against the float64 oracle.
+"""GPU parity on seeded random configurations: the mask builder, the forward (with lse), the
+split-row forward and, for bf16 inputs, the backward, against the float64 oracle.
 
 Each case draws B, H, N (ragged tails and single-block sequences included), d, blk, input
 dtype and structure, top-k or tau (with and without a cap), text tokens, the diagonal, and
@@ -92,7 +92,14 @@ def test_random_config(asa_lib, seed):
     lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
     out = asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp_o, ci_o, cfg.blk, patterns=cfg.patterns, lse=lse)
     torch.cuda.synchronize()
-    compare_outputs(out.cpu().numpy(), O.attention(q64, k64, v64, Meff, cfg.blk), cfg.dtype == "f32", cfg.name)
+    want = O.attention(q64, k64, v64, Meff, cfg.blk)
+    compare_outputs(out.cpu().numpy(), want, cfg.dtype == "f32", cfg.name)
+    # the split-row forward at a random chunk length T (rows of more than T blocks are cut)
+    T = 1 + seed % max(1, cfg.Nb)
+    o_split = asa.asa_attention_fwd_split(xd["q"], xd["k"], xd["v"], rp_o, ci_o, cfg.blk, split_blocks=T,
+                                          patterns=cfg.patterns)
+    torch.cuda.synchronize()
+    compare_outputs(o_split.cpu().numpy(), want, cfg.dtype == "f32", f"{cfg.name} split T={T}")
     L = O.attention_lse(q64, k64, Meff, cfg.blk)
     lg = lse.cpu().numpy().astype(np.float64)
     fin = np.isfinite(L)
