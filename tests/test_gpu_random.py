@@ -1,5 +1,6 @@
-"""GPU parity on seeded random configurations: the mask builder, the forward (with lse), the
-split-row forward and, for bf16 inputs, the backward, against the float64 oracle.
+"""GPU parity on seeded random configurations: the mask builders (adaptive and static-only),
+the forward (with lse), the split-row forward and, for bf16 inputs, the backward, against
+the float64 oracle.
 
 Each case draws B, H, N (ragged tails and single-block sequences included), d, blk, input
 dtype and structure, top-k or tau (with and without a cap), text tokens, the diagonal, and
@@ -81,6 +82,16 @@ def test_random_config(asa_lib, seed):
     amb = O.ambiguous_rows(det["S"], det["P"], mode=cfg.mode, k=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap)
     diff = compare_masks(rp, ci, M, det, amb, cfg.mode, cfg.k, cfg.tau, cfg.k_cap)
     say(f"  mask density {O.density(M):.4f}, ambiguous rows {int(amb.sum())}, differing rows {len(diff)}")
+
+    # the static-only builder on the same patterns (an adaptive head takes the diagonal here:
+    # static calls accept static patterns only), bit-exact
+    if cfg.patterns is not None:
+        spats = [(gen.DIAG, 0) if pid == gen.ADAPTIVE else (pid, prm) for pid, prm in cfg.patterns]
+        srp_t, sci_t = asa.asa_static_mask(cfg.B, cfg.H, cfg.N, cfg.blk, spats, "cuda:0")
+        torch.cuda.synchronize()
+        srp, sci = gpu_csr_rows(srp_t, sci_t)
+        orp, oci = O.to_csr(O.static_mask(cfg.B, cfg.H, cfg.N, cfg.blk, spats))
+        assert np.array_equal(srp, orp) and np.array_equal(sci, oci), "static mask differs from the oracle"
 
     # forward (and lse) on the oracle's mask; skipped heads are all zeros
     Meff = M.copy()
