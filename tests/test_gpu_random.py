@@ -1,6 +1,6 @@
 """GPU parity on seeded random configurations: the mask builders (adaptive and static-only),
-the forward (with lse), the split-row forward and, for bf16 inputs, the backward, against
-the float64 oracle.
+the forward (with lse), the split-row forward, the pattern search and, for bf16 inputs, the
+backward, against the float64 oracle.
 
 Each case draws B, H, N (ragged tails and single-block sequences included), d, blk, input
 dtype and structure, top-k or tau (with and without a cap), text tokens, the diagonal, and
@@ -117,6 +117,24 @@ def test_random_config(asa_lib, seed):
     assert np.array_equal(np.isneginf(lg), ~fin), "lse: -inf pattern differs"
     if fin.any():
         assert float(np.abs(lg[fin] - L[fin]).max()) <= LSE_MAX_ABS
+
+    # the per-head pattern search on random static candidates (even seeds): the loss carries
+    # exactly lam * (1 - S_i) with the oracle's S_i, and the choice follows the selection
+    # rule on the GPU's own losses
+    if seed % 2 == 0:
+        rng = np.random.default_rng(11000 + seed)
+        pool = [(gen.SKIP, 0), (gen.DIAG, 0), (gen.FULL, 0), (gen.MULTIDIAG, int(rng.integers(1, 4 * cfg.blk))),
+                (gen.VSTRIPE, int(rng.integers(0, 3))), (gen.FRAME_TILE, int(rng.integers(1, max(2, cfg.N))))]
+        cands = [pool[int(i)] for i in rng.choice(len(pool), size=int(rng.integers(1, 5)), replace=False)]
+        choice, loss, mse = asa.asa_pattern_search(xd["q"], xd["k"], xd["v"], cfg.blk, cands)
+        torch.cuda.synchronize()
+        S = np.array([O.pattern_sparsity(pid, prm, cfg.N, cfg.blk) for pid, prm in cands])
+        L_np = loss.cpu().numpy()
+        pen = L_np - mse.cpu().numpy()
+        # L - MSE recovers the penalty up to the rounding of the subtraction (a few ulps of L)
+        assert np.all(np.abs(pen - 0.01 * (1.0 - S)[None, :]) <= 1e-15 * (1.0 + np.abs(L_np))), "search penalty"
+        assert np.array_equal(choice.cpu().numpy(), O.select_patterns(loss.cpu().numpy(), 0.1)), "search choice"
+        say(f"  search over {cands}: choices {choice.cpu().numpy().tolist()}")
 
     if cfg.dtype == "bf16" and Meff.any():
         g = torch.from_numpy(np.random.default_rng(seed).standard_normal(tuple(x["q"].shape)).astype(np.float32))
