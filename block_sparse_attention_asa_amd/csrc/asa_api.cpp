@@ -234,7 +234,7 @@ const char* asa_status_string(asa_status st) {
 const char* asa_last_error(void) { return g_last_error; }
 
 int64_t asa_csr_capacity(const asa_shape* shape) {
-  if (!shape || shape->B <= 0 || shape->H <= 0 || shape->N <= 0 || shape->blk <= 0) return -1;
+  if (check_shape(shape, true) != ASA_OK) return -1;   // the shapes the mask builders accept
   const int64_t Nb = num_blocks(shape);
   return (int64_t)shape->B * shape->H * Nb * Nb;
 }

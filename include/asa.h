@@ -132,7 +132,8 @@ const char* asa_status_string(asa_status status);
 const char* asa_last_error(void);
 
 /* Number of col_idx elements the mask builders require: B*H*Nb*Nb (the worst case, since
- * the kept count is known only on the device).  Returns -1 for an invalid shape. */
+ * the kept count is known only on the device).  Returns -1 for a shape the mask builders
+ * reject (see the status codes), with the reason in asa_last_error(). */
 int64_t asa_csr_capacity(const asa_shape* shape);
 
 /* Workspace bytes for asa_build_mask (pooled Q and K, row bitmasks and counts).  Returns 0 for an invalid shape. */

@@ -66,6 +66,8 @@ def test_capacity_and_workspace_sizes():
     assert asa.lib.asa_static_mask_workspace_size(ctypes.byref(s)) >= rows * 8
     assert asa.lib.asa_build_mask_workspace_size(ctypes.byref(_shape(d=96))) == 0
     assert asa.lib.asa_csr_capacity(None) == -1
+    assert asa.lib.asa_csr_capacity(ctypes.byref(_shape(d=96))) == -1          # shapes the builders reject
+    assert asa.lib.asa_csr_capacity(ctypes.byref(_shape(N=64 * 1025, blk=64))) == -1   # Nb > 1024
 
 
 @pytest.mark.parametrize("shape,code", [
