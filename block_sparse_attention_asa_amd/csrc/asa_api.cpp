@@ -213,7 +213,7 @@ size_t split_workspace_layout(const asa_shape* s, int split_max, float** part_o,
 
 extern "C" {
 
-int32_t asa_version(void) { return 10400; }
+int32_t asa_version(void) { return 10500; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {

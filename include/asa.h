@@ -122,7 +122,8 @@ typedef struct asa_csr {
 
 /* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order;
  * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split; 1.4.0 added
- * ASA_PAT_FRAME_TILE. */
+ * ASA_PAT_FRAME_TILE; 1.5.0: asa_attention_bwd follows asa_csr.order, and asa_csr_capacity
+ * returns -1 for every shape the mask builders reject. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */

@@ -281,4 +281,4 @@ def test_plain_c_client_links_and_calls(tmp_path):
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10400
+    assert asa.lib.asa_version() >= 10500
