@@ -282,3 +282,12 @@ def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
     assert asa.lib.asa_version() >= 10500
+
+
+def test_invalid_shape_left_to_the_builder():
+    """For a shape the builders reject, the binding allocates no CSR of its own size: the
+    builder call validates the shape first and raises AsaError with its status."""
+    rp, ci = asa._alloc_csr(1, 1, 1560, 96, "cpu")
+    assert rp.numel() == 1 and ci.numel() == 1
+    rp, ci = asa._alloc_csr(1, 2, 1024, 64, "cpu")
+    assert rp.numel() == 2 * 16 + 1 and ci.numel() == 2 * 16 * 16
