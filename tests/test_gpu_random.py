@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 LSE_MAX_ABS = 2.0 ** -8 + 1e-4
 GRAD_MAX_REL, GRAD_MEAN_REL = 2e-2, 5e-3
-N_CASES = 32
+N_CASES = 128
 
 
 def _random_config(seed):
