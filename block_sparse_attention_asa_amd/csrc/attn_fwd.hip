@@ -8,7 +8,8 @@
 // "四种注意力模式" table) produce zeros.
 //
 // Work decomposition: one workgroup per (b, h, query block r); BLK/32 wavefronts, each
-// owning 32 query rows.  Kept key blocks are consumed in 64-key steps: K and V of a step
+// owning 32 query rows.  Kept key blocks are consumed in steps of 32 or 64 keys (chosen per
+// launch): K and V of a step
 // land row-major (16-byte granules swizzled) in one slot of a two-slot LDS ring by direct
 // global -> LDS transfers, and each wavefront computes
 //     S^T = K_c Q^T          (32x32x16 bf16 MFMA, or 32x32x2 f32 MFMA for fp32 inputs)
@@ -35,12 +36,15 @@ namespace {
 // arithmetic).
 // kSplit: the launch cuts long rows into chunks (meta.split_blocks > 0); a separate
 // instantiation keeps the registers of the plain kernel untouched.
-template <typename T, typename TO, int D, int BLK, bool kSplit>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(
+// KT: keys per step.  32-key steps keep a d = 128 kernel under 168 registers and 32 KB of
+// LDS, so three wavefronts share a SIMD; launches with enough rows to fill those slots use
+// them.  64-key steps do more work per barrier, which wins when a compute unit holds fewer
+// workgroups (small launches, d = 64).
+template <typename T, typename TO, int D, int BLK, int KT, bool kSplit>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 32 ? 3 : 2))) void attn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, TO* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int N, int Nb,
     int total_rows, float scale_log2, AttnArgs meta) {
-  constexpr int KT = 64;           // keys per step
   constexpr int kSteps = BLK / KT; // steps per key block
   constexpr int kWaves = BLK / 32;
   constexpr int NT = 64 * kWaves;
@@ -407,21 +411,34 @@ __global__ __launch_bounds__(256) void split_combine_kernel(AttnArgs a, int tota
   }
 }
 
-template <typename T, typename TO, int D, int BLK>
-hipError_t launch_typed(const AttnArgs& a, hipStream_t s) {
+// Rows from which a d = 128, 128-query-block launch takes 32-key steps: three workgroups
+// per compute unit.  The split path follows the same rule, so rows it leaves whole match
+// the plain kernel bit for bit.
+constexpr int kShortStepRows = 768;
+
+template <typename T, typename TO, int D, int BLK, int KT>
+hipError_t launch_kt(const AttnArgs& a, hipStream_t s) {
   const int total = a.B * a.H * a.Nb;
   if (a.split_blocks > 0) {
     // 8 equal shares of (rows of the XCD's range) x (chunks per row)
     const long long items = (long long)kXcds * ((total + kXcds - 1) / kXcds) * a.split_max;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK, true>), dim3((unsigned)items), dim3(BLK * 2), 0, s,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK, KT, true>), dim3((unsigned)items), dim3(BLK * 2), 0, s,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<TO*>(a.o), a.row_ptr, a.col_idx, a.H, a.N, a.Nb, total, a.scale_log2, a);
   } else {
-    hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK, false>), dim3((unsigned)total), dim3(BLK * 2), 0, s,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, TO, D, BLK, KT, false>), dim3((unsigned)total), dim3(BLK * 2), 0, s,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                        static_cast<TO*>(a.o), a.row_ptr, a.col_idx, a.H, a.N, a.Nb, total, a.scale_log2, a);
   }
   return hipGetLastError();
+}
+
+template <typename T, typename TO, int D, int BLK>
+hipError_t launch_typed(const AttnArgs& a, hipStream_t s) {
+  if constexpr (D == 128 && BLK == 128) {
+    if ((long long)a.B * a.H * a.Nb >= kShortStepRows) return launch_kt<T, TO, D, BLK, 32>(a, s);
+  }
+  return launch_kt<T, TO, D, BLK, 64>(a, s);
 }
 
 template <typename T, typename TO>
