@@ -569,6 +569,140 @@ def check_search_follows_table3_trends():
     assert kept[(0.01, 0.15)] < kept[(0.01, 0.1)] < kept[(0.01, 0.05)], kept
 
 
+# ------------------------------------------------------------------ near-tie rule pins
+def _row_from_sorted_scores(vals, perm):
+    """A score row whose rank order is `perm` and whose sorted scores are `vals`."""
+    s = np.empty(len(vals))
+    s[np.asarray(perm)] = vals
+    return s
+
+
+def _filler_rows(nb):
+    """Score rows with gaps of at least 0.5 everywhere (never near a tie)."""
+    return np.stack([np.roll(np.arange(nb, dtype=np.float64) * 0.5, i) for i in range(nb)])
+
+
+def _amb_single(s_row, **kw):
+    """The near-tie flag of one planted row, placed as row 0 of a square score matrix."""
+    s_row = np.asarray(s_row, dtype=np.float64)
+    S = _filler_rows(s_row.shape[0])
+    S[0] = s_row
+    S = S[None, None]
+    return bool(O.ambiguous_rows(S, O.block_softmax(S), **kw)[0, 0, 0])
+
+
+def check_ambiguous_rows_planted():
+    """The near-tie rule (a row may differ between two correct implementations only if the
+    last kept and first dropped candidates differ in block score by under 1e-6, or the
+    cumulative mass next to the stopping point is within 1e-6 of tau), on planted rows.
+
+    Every expectation below follows from the rule's wording, not from the oracle: the
+    gaps are placed in S (flag below 1e-6, none at 2e-6, including at small P where P
+    gaps are far below 1e-6), only at the selection edge (near-ties one place before or
+    after the edge do not flag), and at the prefix masses just before and at the stopping
+    point in cumulative-mass mode.  Rows keeping no candidate or every candidate have no
+    edge and never flag.
+    """
+    perm = [5, 2, 7, 0, 3, 6, 1, 4]                      # rank order of the planted rows
+    base = np.array([4.0, 3.0, 2.0, 1.0, 0.0, -1.0, -2.0, -3.0])
+
+    def topk_row(edge_gap, at=2, lift=0.0):
+        v = base.copy() + lift
+        v[at + 1] = v[at] - edge_gap                     # gap between rank `at` and `at`+1
+        return _row_from_sorted_scores(v, perm)
+
+    k = 3                                                # edge between rank 2 and rank 3
+    assert _amb_single(topk_row(5e-7), mode=O.TOPK, k=k)
+    assert not _amb_single(topk_row(2e-6), mode=O.TOPK, k=k)
+    # the same gaps far down the softmax (P ~ 1e-6 and below): P gaps are ~1e-12, so
+    # only gaps measured in S decide
+    v = base.copy()
+    v[2:] -= 14.0                                        # ranks 2.. at P ~ 1e-6 and below
+    v[3] = v[2] - 2e-6
+    assert not _amb_single(_row_from_sorted_scores(v, perm), mode=O.TOPK, k=k)
+    v[3] = v[2] - 5e-7
+    assert _amb_single(_row_from_sorted_scores(v, perm), mode=O.TOPK, k=k)
+    # near-ties one place before and one place after the edge do not flag
+    vb = base.copy()                                     # ranks 1, 2 (both kept)
+    vb[2] = vb[1] - 1e-9
+    assert not _amb_single(_row_from_sorted_scores(vb, perm), mode=O.TOPK, k=k)
+    va = base.copy()
+    va[4] = va[3] - 1e-9                                 # ranks 3, 4 (both dropped)
+    assert not _amb_single(_row_from_sorted_scores(va, perm), mode=O.TOPK, k=k)
+    # no edge: k = 0 keeps nothing, k >= Nb keeps everything (exact ties everywhere)
+    flat = np.zeros(8)
+    assert not _amb_single(flat, mode=O.TOPK, k=0)
+    assert not _amb_single(flat, mode=O.TOPK, k=8)
+    assert not _amb_single(flat, mode=O.TOPK, k=20)
+    assert _amb_single(flat, mode=O.TOPK, k=4)
+
+    # cumulative-mass mode: P chosen directly, S = log P (softmax gives P back)
+    p = np.array([0.4, 0.25, 0.15, 0.1, 0.06, 0.04])
+    perm6 = [3, 0, 5, 1, 4, 2]
+    s6 = _row_from_sorted_scores(np.log(p), perm6)
+    cs = np.cumsum(p)
+    tau_far = cs[2] + 0.02                               # between cs[2] and cs[3], far from both
+    assert not _amb_single(s6, mode=O.TAU, tau=tau_far)
+    # mass at the stopping point within 3e-7 above tau: m = 3, cs[m-1] - tau = 3e-7
+    assert _amb_single(s6, mode=O.TAU, tau=cs[2] - 3e-7)
+    # mass just before the stopping point within 3e-7 below tau: m = 4, tau - cs[m-2] = 3e-7
+    assert _amb_single(s6, mode=O.TAU, tau=cs[2] + 3e-7)
+    # the same distances at 2e-6 do not flag
+    assert not _amb_single(s6, mode=O.TAU, tau=cs[2] - 2e-6)
+    assert not _amb_single(s6, mode=O.TAU, tau=cs[2] + 2e-6)
+    # mass one place after the stopping point near tau is no edge: m = 2 here
+    # (cs[1] >= tau), and cs[2] sits 3e-7 from a second threshold that is not tau
+    assert not _amb_single(s6, mode=O.TAU, tau=cs[1] - 0.01)
+    # tau above the total: every candidate kept, no edge
+    assert not _amb_single(s6, mode=O.TAU, tau=1.5)
+    # the cap sets the edge: natural m = 4, cap 2, ranks 1 and 2 within 5e-7 in S
+    pc = np.array([0.4, 0.2, 0.2 * np.exp(-5e-7), 0.1, 0.06, 0.04])
+    pc /= pc.sum()
+    sc = _row_from_sorted_scores(np.log(pc), perm6)
+    assert _amb_single(sc, mode=O.TAU, tau=0.85, k_cap=2)
+    pc2 = np.array([0.4, 0.2, 0.2 * np.exp(-2e-6), 0.1, 0.06, 0.04])
+    sc2 = _row_from_sorted_scores(np.log(pc2 / pc2.sum()), perm6)
+    assert not _amb_single(sc2, mode=O.TAU, tau=0.85, k_cap=2)
+
+    # many rows at once keep their own flags (no leakage across rows, heads, batches)
+    rows = [topk_row(5e-7), topk_row(2e-6), topk_row(1e-3), topk_row(3e-7)]
+    S = np.stack([_filler_rows(8)] * 4)
+    for i, row in enumerate(rows):
+        S[i, 5] = row
+    S = S.reshape(2, 2, 8, 8)
+    got = O.ambiguous_rows(S, O.block_softmax(S), mode=O.TOPK, k=k).reshape(4, 8)
+    assert got[:, 5].tolist() == [True, False, False, True]
+    assert not got[:, :5].any() and not got[:, 6:].any()
+
+
+def check_attention_block_matches_sdpa_and_full():
+    """attention_block (the outputs of one query block) equals torch SDPA run on that
+    block's queries against the union of its kept key blocks (a library routine), and the
+    matching slice of the full masked attention, on ragged blocks and an empty row."""
+    B, H, N, d, blk = 2, 2, 230, 16, 64                  # 4 blocks, last one 38 tokens
+    q, k, v = _qkv(B, H, N, d, 61, scale=1.5)
+    Nb = O.num_blocks(N, blk)
+    rng = RNG(62)
+    M = rng.random((B, H, Nb, Nb)) < 0.5
+    M[1, 0, 2, :] = False                                # an empty row
+    M[0, 1, 3, :] = True                                 # a full ragged row
+    full = O.attention(q, k, v, M, blk)
+    for b in range(B):
+        for h in range(H):
+            for r in range(Nb):
+                lo, hi = O.block_range(r, N, blk)
+                got = O.attention_block(q, k, v, M, blk, b, h, r)
+                assert got.shape == (hi - lo, d)
+                cols = [c for c in range(Nb) if M[b, h, r, c]]
+                if not cols:
+                    assert np.all(got == 0.0)
+                else:
+                    J = np.concatenate([np.arange(*O.block_range(c, N, blk)) for c in cols])
+                    ref = _sdpa(q[b, h, lo:hi][None], k[b, h, J][None], v[b, h, J][None])[0]
+                    assert np.allclose(got, ref, atol=1e-12, rtol=0)
+                assert np.array_equal(got, full[b, h, lo:hi])
+
+
 ALL_CHECKS = [
     check_dense_equals_sdpa, check_block_diagonal_equals_independent_blocks,
     check_weights_sum_to_one, check_identical_keys_give_mean_of_v,
@@ -584,4 +718,5 @@ ALL_CHECKS = [
     check_pattern_sparsity_token_pairs, check_pattern_mse_matches_torch,
     check_pattern_uniform_attention_closed_form, check_select_rule_cases,
     check_search_follows_table3_trends,
+    check_ambiguous_rows_planted, check_attention_block_matches_sdpa_and_full,
 ]

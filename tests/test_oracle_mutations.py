@@ -180,6 +180,50 @@ def _sparsity_tile_count(pattern, param, N, blk):
     return 1.0 - kept / float(Nb * Nb)
 
 
+def _ambiguous_variant(which):
+    def f(S, P, *, mode, k=0, tau=0.0, k_cap=0, gap=core.AMBIGUITY_GAP):
+        B, H, Nb, _ = S.shape
+        amb = np.zeros((B, H, Nb), dtype=bool)
+        if which == "all":
+            amb[:] = True
+            return amb
+        for b in range(B):
+            for h in range(H):
+                for r in range(Nb):
+                    p = P[b, h, r]
+                    order = core.rank_order(p)
+                    m = core.adaptive_count(p, order, mode, k, tau, k_cap)
+                    vals = p if which == "gap_on_p" else S[b, h, r]
+                    e = m + 1 if which == "edge_off_by_one" else m
+                    flag = False
+                    if 0 < e < Nb:
+                        flag = abs(vals[order[e - 1]] - vals[order[e]]) < gap
+                    if mode == core.TAU and not flag:
+                        cs = np.cumsum(p[order])
+                        ts = (m - 1, m) if which == "tau_index_off_by_one" else (m - 2, m - 1)
+                        for t in ts:
+                            if 0 <= t < Nb and abs(cs[t] - tau) < gap:
+                                flag = True
+                    amb[b, h, r] = flag
+        return amb
+    return f
+
+
+def _attention_block_variant(which):
+    def f(Q, K, V, M, blk, b, h, r):
+        N, d = Q.shape[2], Q.shape[3]
+        rr = min(r + 1, core.num_blocks(N, blk) - 1) if which == "next_block_queries" else r
+        lo, hi = core.block_range(rr, N, blk)
+        J = core.kept_tokens(M[b, h, r], N, blk)
+        if J.size == 0:
+            return np.zeros((hi - lo, d))
+        q = Q[b, h, lo:hi]
+        s = (q @ K[b, h, J].T) / (1.0 if which == "no_scale" else np.sqrt(d))
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        return (e @ V[b, h, J]) / e.sum(axis=1, keepdims=True)
+    return f
+
+
 MUTATIONS = {
     "pool_sum_not_mean": ("pool", _pool_sum),
     "pool_zero_padded_partial_block": ("pool", _pool_zero_padded),
@@ -206,6 +250,12 @@ MUTATIONS = {
     "search_mse_pooled_over_heads": ("pattern_mse", _mse_pooled_heads),
     "search_mse_sum_not_mean": ("pattern_mse", _mse_sum),
     "search_sparsity_counts_tiles": ("pattern_sparsity", _sparsity_tile_count),
+    "near_tie_gap_on_p_not_s": ("ambiguous_rows", _ambiguous_variant("gap_on_p")),
+    "near_tie_edge_off_by_one": ("ambiguous_rows", _ambiguous_variant("edge_off_by_one")),
+    "near_tie_tau_prefix_off_by_one": ("ambiguous_rows", _ambiguous_variant("tau_index_off_by_one")),
+    "near_tie_every_row_flagged": ("ambiguous_rows", _ambiguous_variant("all")),
+    "attention_block_next_block_queries": ("attention_block", _attention_block_variant("next_block_queries")),
+    "attention_block_missing_scale": ("attention_block", _attention_block_variant("no_scale")),
 }
 
 
