@@ -187,6 +187,11 @@ def _csr_buffers(out, with_order, B, H, N, blk, device):
             raise ValueError("out must be (row_ptr, col_idx) or (row_ptr, col_idx, order)")
         row_ptr, col_idx = out[0], out[1]
         order = out[2] if len(out) == 3 else None
+        _require_device(row_ptr, col_idx)
+        if row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+            raise TypeError("row_ptr and col_idx must be int32")
+        if row_ptr.numel() != B * H * num_blocks(N, blk) + 1:
+            raise ValueError("row_ptr length does not match [B, H, Nb] rows")
     else:
         row_ptr, col_idx = _alloc_csr(B, H, N, blk, device)
         order = None
@@ -276,6 +281,8 @@ def asa_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, row_ptr
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     _require_device(out)
+    if tuple(out.shape) != (B, H, N, d):
+        raise ValueError(f"out must have shape {(B, H, N, d)}, got {tuple(out.shape)}")
     o_code = _dtype_code(out)
     if order is not None:
         _require_device(order)
@@ -318,6 +325,8 @@ def asa_attention_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, r
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     _require_device(out)
+    if tuple(out.shape) != (B, H, N, d):
+        raise ValueError(f"out must have shape {(B, H, N, d)}, got {tuple(out.shape)}")
     if order is not None:
         _require_device(order)
         if order.dtype != torch.int32 or order.numel() != row_ptr.numel() - 1:

@@ -95,3 +95,35 @@ def test_order_argument_checks(asa_lib):
     with pytest.raises(ValueError):
         asa.asa_static_mask(cfg.B, cfg.H, cfg.N, cfg.blk, cfg.head_patterns(), "cuda:0",
                             out=(rp, ci, bad))
+
+
+@pytest.mark.gpu
+def test_csr_and_output_buffer_checks(asa_lib):
+    """Caller-supplied CSR and output buffers are checked before anything is launched:
+    host tensors, wrong dtypes, a short row_ptr and a mis-shaped output all raise."""
+    asa = asa_lib
+    cfg = gen.STATIC
+    pats = cfg.head_patterns()
+    rp, ci = asa.asa_static_mask(cfg.B, cfg.H, cfg.N, cfg.blk, pats, "cuda:0")
+    x = to_device(gen.make_inputs(cfg))
+    dev = "cuda:0"
+    cases = [
+        (rp.cpu(), ci),                                              # host row_ptr
+        (rp, ci.cpu()),                                              # host col_idx
+        (rp.to(torch.int64), ci),                                    # wrong dtype
+        (rp, ci.to(torch.int64)),
+        (torch.zeros(rp.numel() - 1, dtype=torch.int32, device=dev), ci),   # short row_ptr
+    ]
+    for out in cases:
+        with pytest.raises((ValueError, TypeError)):
+            asa.asa_static_mask(cfg.B, cfg.H, cfg.N, cfg.blk, pats, dev, out=out)
+        with pytest.raises((ValueError, TypeError)):
+            asa.asa_build_mask(x["q"], x["k"], cfg.blk, asa.TOPK, k_top=2, out=out)
+    B, H, N, d = x["q"].shape
+    for shape in [(B, H, N - 1, d), (B, H, N, d // 2), (B * H * N * d,)]:
+        small = torch.empty(shape, dtype=torch.float32, device=dev)
+        with pytest.raises(ValueError):
+            asa.asa_attention_fwd(x["q"], x["k"], x["v"], rp, ci, cfg.blk, out=small)
+        with pytest.raises(ValueError):
+            asa.asa_attention_fwd_split(x["q"], x["k"], x["v"], rp, ci, cfg.blk, out=small)
+    torch.cuda.synchronize()

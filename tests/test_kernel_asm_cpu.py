@@ -8,9 +8,9 @@ The compiler does not see inside them, so they must not touch state it relies on
   * M0 is written only inside those blocks (the compiler never reads a value it set);
   * no 64-bit base pointer is rebuilt with a sign-extending s_bfe_i64.
 """
+import importlib.util
 import os
 import re
-import shutil
 import subprocess
 
 import pytest
@@ -18,6 +18,17 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRCS = [os.path.join(ROOT, "block_sparse_attention_asa_amd", "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip")]
 HIPCC = "/opt/rocm/bin/hipcc"
+
+
+def _build_module():
+    """The library's build script, loaded by path (importing the package needs the built
+    library), so that the checked assembly comes from the flags the library ships with."""
+    spec = importlib.util.spec_from_file_location(
+        "_asa_build_flags", os.path.join(ROOT, "block_sparse_attention_asa_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
 
 ALLOWED = {"s_mov_b32", "s_nop", "global_load_lds_dwordx4", "v_max3_f32"}
 
@@ -27,10 +38,9 @@ def asm_text(request, tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("asm") / (os.path.basename(request.param) + ".s")
-    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", f"-I{ROOT}/include",
-           f"-I{ROOT}/block_sparse_attention_asa_amd/csrc", "-x", "hip", "-S", "--offload-device-only",
-           request.param, "-o", str(out)]
+    b = _build_module()
+    flags = [f for f in b.COMMON if f != "-fPIC"] + b.EXTRA.get(os.path.basename(request.param), [])
+    cmd = [HIPCC, *flags, "-x", "hip", "-S", "--offload-device-only", request.param, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out.read_text()
 
