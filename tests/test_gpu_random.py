@@ -146,3 +146,72 @@ def test_random_config(asa_lib, seed):
         _grad_close(dq, rdq, "dQ")
         _grad_close(dk, rdk, "dK")
         _grad_close(dv, rdv, "dV")
+
+
+# Launches of at least 768 query-block rows at d = 128, blk = 128 take the 32-key-step
+# kernel; the family above stays below that, so a second family draws such launches.
+N_LARGE_CASES = 12
+
+
+def _random_large_config(seed):
+    rng = np.random.default_rng(17000 + seed)
+    Nb = int(rng.integers(48, 97))
+    B = int(rng.integers(1, 3))
+    H = max(int(rng.integers(4, 13)), -(-768 // (B * Nb)))
+    N = Nb * 128 - int(rng.integers(0, 128))
+    mode = gen.TOPK if rng.random() < 0.6 else gen.TAU
+    patterns = None
+    if rng.random() < 0.5:
+        choices = [(gen.ADAPTIVE, 0), (gen.SKIP, 0), (gen.DIAG, 0), (gen.MULTIDIAG, int(rng.integers(1, 2048))),
+                   (gen.VSTRIPE, int(rng.integers(0, 3))), (gen.FRAME_TILE, int(rng.integers(128, 4096)))]
+        patterns = [choices[int(rng.integers(0, len(choices)))] for _ in range(H)]
+    return gen.Config(name=f"random_large_{seed}", seed=19000 + seed, B=B, H=H, N=N, d=128, blk=128,
+                      dtype="bf16" if rng.random() < 0.75 else "f32", frames=1, Hs=1, Ws=N,
+                      structure=str(rng.choice(["none", "smooth"])), kind="adaptive", mode=mode,
+                      k=int(rng.integers(1, 10)), tau=float(rng.uniform(0.3, 0.95)),
+                      k_cap=int(rng.integers(4, 16)) if mode == gen.TAU else 0,
+                      keep_diag=int(rng.integers(0, 2)), patterns=patterns)
+
+
+@pytest.mark.parametrize("seed", range(N_LARGE_CASES))
+def test_random_large_launch(asa_lib, seed):
+    """Mask, forward (with lse) and split forward over whole outputs at >= 768 rows."""
+    asa = asa_lib
+    cfg = _random_large_config(seed)
+    assert cfg.B * cfg.H * cfg.Nb >= 768
+    say(f"case {cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} rows={cfg.B * cfg.H * cfg.Nb} {cfg.dtype} "
+        f"{cfg.structure} mode={cfg.mode} k={cfg.k} tau={cfg.tau:.3f} cap={cfg.k_cap} diag={cfg.keep_diag} "
+        f"patterns={cfg.patterns}")
+    x = gen.make_inputs(cfg)
+    xd = to_device(x)
+    q64, k64, v64 = oracle_inputs(x)
+    M, det = O.build_mask(q64, k64, cfg.blk, mode=cfg.mode, k=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap,
+                          keep_diag=cfg.keep_diag, patterns=cfg.patterns, return_details=True)
+    rp_t, ci_t = asa.asa_build_mask(xd["q"], xd["k"], cfg.blk, cfg.mode, k_top=cfg.k, tau=cfg.tau,
+                                    k_cap=cfg.k_cap, keep_diag=cfg.keep_diag, patterns=cfg.patterns)
+    torch.cuda.synchronize()
+    rp, ci = gpu_csr_rows(rp_t, ci_t)
+    amb = O.ambiguous_rows(det["S"], det["P"], mode=cfg.mode, k=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap)
+    diff = compare_masks(rp, ci, M, det, amb, cfg.mode, cfg.k, cfg.tau, cfg.k_cap)
+    say(f"  mask density {O.density(M):.4f}, ambiguous rows {int(amb.sum())}, differing rows {len(diff)}")
+    Meff = M.copy()
+    if cfg.patterns is not None:
+        for h, (pid, _) in enumerate(cfg.patterns):
+            if pid == O.SKIP:
+                Meff[:, h] = False
+    rp_o, ci_o = csr_to_device(M)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device="cuda:0")
+    out = asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], rp_o, ci_o, cfg.blk, patterns=cfg.patterns, lse=lse)
+    T = 2 + seed % 5
+    o_split = asa.asa_attention_fwd_split(xd["q"], xd["k"], xd["v"], rp_o, ci_o, cfg.blk, split_blocks=T,
+                                          patterns=cfg.patterns)
+    torch.cuda.synchronize()
+    want = O.attention(q64, k64, v64, Meff, cfg.blk)
+    compare_outputs(out.cpu().numpy(), want, cfg.dtype == "f32", cfg.name)
+    compare_outputs(o_split.cpu().numpy(), want, cfg.dtype == "f32", f"{cfg.name} split T={T}")
+    L = O.attention_lse(q64, k64, Meff, cfg.blk)
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(L)
+    assert np.array_equal(np.isneginf(lg), ~fin), "lse: -inf pattern differs"
+    if fin.any():
+        assert float(np.abs(lg[fin] - L[fin]).max()) <= LSE_MAX_ABS
