@@ -6,6 +6,7 @@ fallback: importing this package fails if the built library is missing.
 
 Entry points (same names as the C ABI in include/asa.h):
     asa_build_mask(q, k, blk, mode, ...)   -> (row_ptr, col_idx)
+    asa_build_mask_noalloc(q, k, blk, mode, out=(row_ptr, col_idx), ...) -> same, no allocation
     asa_static_mask(B, H, N, blk, patterns, device) -> (row_ptr, col_idx)
     asa_attention_fwd(q, k, v, row_ptr, col_idx, blk, ...) -> O
     asa_attention_fwd_split(q, k, v, row_ptr, col_idx, blk, split_blocks=...) -> O
@@ -56,6 +57,9 @@ EXPORTS = {
                                       ctypes.POINTER(asa_adaptive), ctypes.POINTER(asa_head_pattern),
                                       ctypes.POINTER(asa_csr), ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p]),
+    "asa_build_mask_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(asa_shape),
+                                              ctypes.POINTER(asa_adaptive), ctypes.POINTER(asa_head_pattern),
+                                              ctypes.POINTER(asa_csr), ctypes.c_void_p]),
     "asa_static_mask": (ctypes.c_int, [ctypes.POINTER(asa_shape), ctypes.POINTER(asa_head_pattern),
                                        ctypes.POINTER(asa_csr), ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]),
@@ -235,6 +239,32 @@ def asa_build_mask(q: torch.Tensor, k: torch.Tensor, blk: int, mode: int, *, k_t
     _check(lib.asa_build_mask(q.data_ptr(), k.data_ptr(), ctypes.byref(shp), ctypes.byref(ad),
                               pats, ctypes.byref(csr), workspace.data_ptr(), workspace.numel(),
                               _stream(q.device, stream)), "asa_build_mask")
+    return (row_ptr, col_idx) if order is None else (row_ptr, col_idx, order)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def asa_build_mask_noalloc(q: torch.Tensor, k: torch.Tensor, blk: int, mode: int, *,
+                           out: Tuple[torch.Tensor, ...], k_top: int = 0, tau: float = 0.0,
+                           k_cap: int = 0, n_text: int = 0, keep_diag: int = 1,
+                           patterns: Optional[Sequence[Tuple[int, int]]] = None, stream=None):
+    """asa_build_mask into caller-supplied CSR buffers `out` = (row_ptr, col_idx[, order]),
+    with the library's static device scratch as workspace: the call allocates nothing.
+    Shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES raise AsaError."""
+    _require_device(q, k)
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must have the same shape and dtype")
+    if out is None:
+        raise ValueError("out = (row_ptr, col_idx[, order]) is required: this call allocates nothing")
+    shp = _shape_of(q, blk)
+    B, H, N, _ = q.shape
+    row_ptr, col_idx, order = _csr_buffers(out, False, B, H, N, blk, q.device)
+    csr = _csr_struct(row_ptr, col_idx, order)
+    ad = asa_adaptive(mode, k_top, tau, k_cap, n_text, keep_diag)
+    _check(lib.asa_build_mask_noalloc(q.data_ptr(), k.data_ptr(), ctypes.byref(shp), ctypes.byref(ad),
+                                      _patterns(patterns, H), ctypes.byref(csr), _stream(q.device, stream)),
+           "asa_build_mask_noalloc")
     return (row_ptr, col_idx) if order is None else (row_ptr, col_idx, order)
 
 
@@ -437,7 +467,7 @@ def asa_pattern_search(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk: i
     return choice, loss, mse
 
 
-__all__ = ["asa_build_mask", "asa_static_mask", "asa_attention_fwd", "asa_attention_fwd_split",
+__all__ = ["asa_build_mask", "asa_build_mask_noalloc", "NOALLOC_SCRATCH_BYTES", "asa_static_mask", "asa_attention_fwd", "asa_attention_fwd_split",
            "asa_attention_bwd", "asa_pattern_search",
            "asa_csr_capacity",
            "AsaError", "lib", "LIB_PATH", "EXPORTS", "num_blocks",

@@ -10,6 +10,8 @@
 #include "asa.h"
 #include "asa_internal.h"
 
+static_assert(ASA_NOALLOC_SCRATCH_BYTES == asa::kNoAllocScratchBytes, "scratch size in asa.h and the library differ");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -213,7 +215,7 @@ size_t split_workspace_layout(const asa_shape* s, int split_max, float** part_o,
 
 extern "C" {
 
-int32_t asa_version(void) { return 10500; }
+int32_t asa_version(void) { return 10600; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {
@@ -249,10 +251,12 @@ size_t asa_static_mask_workspace_size(const asa_shape* shape) {
   return asa::mask_workspace_layout(geom_of(shape), false, nullptr, nullptr);
 }
 
-asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
-                          const asa_adaptive* ad, const asa_head_pattern* patterns,
-                          const asa_csr* out, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+// asa_build_mask and its variant without allocation (no_alloc: the workspace is the
+// device's static scratch array, found after every argument check has passed).
+static asa_status build_mask_impl(const void* Q, const void* K, const asa_shape* shape,
+                                  const asa_adaptive* ad, const asa_head_pattern* patterns,
+                                  const asa_csr* out, void* workspace, size_t workspace_bytes,
+                                  void* stream, bool no_alloc) {
   g_last_error[0] = '\0';
   asa_status st = check_shape(shape, true);
   if (st != ASA_OK) return st;
@@ -272,6 +276,14 @@ asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
   if ((st = check_csr_out(shape, out)) != ASA_OK) return st;
   const asa::MaskGeom g = geom_of(shape);
   const size_t need = asa::mask_workspace_layout(g, true, nullptr, nullptr);
+  if (no_alloc) {
+    if (need > asa::kNoAllocScratchBytes)
+      return fail(ASA_ERR_WORKSPACE, "shape needs %zu workspace bytes, more than the %zu-byte static scratch", need,
+                  asa::kNoAllocScratchBytes);
+    hipError_t e = asa::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    workspace_bytes = asa::kNoAllocScratchBytes;
+  }
   if ((st = check_workspace(workspace, workspace_bytes, need)) != ASA_OK) return st;
 
   asa::MaskWorkspace ws;
@@ -289,6 +301,19 @@ asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
   if ((e = asa::launch_rank(g, p, heads, ws, s)) != hipSuccess) return hip_fail(e, "rank");
   if ((e = asa::launch_csr(g, ws, out->row_ptr, out->col_idx, out->order, s)) != hipSuccess) return hip_fail(e, "csr");
   return ASA_OK;
+}
+
+asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
+                          const asa_adaptive* ad, const asa_head_pattern* patterns,
+                          const asa_csr* out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return build_mask_impl(Q, K, shape, ad, patterns, out, workspace, workspace_bytes, stream, false);
+}
+
+asa_status asa_build_mask_noalloc(const void* Q, const void* K, const asa_shape* shape,
+                                  const asa_adaptive* ad, const asa_head_pattern* patterns,
+                                  const asa_csr* out, void* stream) {
+  return build_mask_impl(Q, K, shape, ad, patterns, out, nullptr, 0, stream, true);
 }
 
 asa_status asa_static_mask(const asa_shape* shape, const asa_head_pattern* patterns,

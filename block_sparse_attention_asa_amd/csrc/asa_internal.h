@@ -51,6 +51,12 @@ struct MaskWorkspace {
 
 size_t mask_workspace_layout(const MaskGeom& g, bool adaptive, MaskWorkspace* ws, void* base);
 
+// Device scratch of asa_build_mask_noalloc: a static device array of this many bytes on
+// every GPU the library runs on.  noalloc_scratch returns its address on the current
+// device (looked up once per device, then cached).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Mask pipeline stages (enqueue only; return the launch status).
 hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& g,
                        const MaskWorkspace& ws, hipStream_t s);

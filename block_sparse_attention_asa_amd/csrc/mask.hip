@@ -23,10 +23,42 @@
 //   csr_fill_kernel  one wavefront per row: bitmask -> ascending col_idx.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "asa_internal.h"
 #include "order.h"
 
+// Workspace of asa_build_mask_noalloc, for callers that cannot allocate device memory.
+// Each GPU holds its own copy until the process ends.  Host code never passes this name
+// to a kernel (on the host it is only a stand-in for the symbol): it takes the device
+// address from noalloc_scratch below.
+static __device__ __align__(256) unsigned char scratch[asa::kNoAllocScratchBytes];
+
 namespace asa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 constexpr int kThreads = 256;

@@ -24,7 +24,8 @@
  *    memory read during the call only.
  *  - Ownership: the caller allocates every buffer (outputs and workspace).  The library
  *    allocates nothing, keeps no state between calls and never synchronizes: all work is
- *    enqueued on `stream` (a hipStream_t; NULL means the default stream).
+ *    enqueued on `stream` (a hipStream_t; NULL means the default stream).  The one
+ *    exception is asa_build_mask_noalloc, whose workspace is a static device array.
  *  - Errors: arguments are validated on the host before anything is enqueued; an invalid
  *    call returns a negative asa_status, enqueues nothing, and asa_last_error() returns a
  *    thread-local message.  Launch failures return ASA_ERR_HIP.  Faults inside kernels
@@ -123,7 +124,7 @@ typedef struct asa_csr {
 /* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order;
  * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split; 1.4.0 added
  * ASA_PAT_FRAME_TILE; 1.5.0: asa_attention_bwd follows asa_csr.order, and asa_csr_capacity
- * returns -1 for every shape the mask builders reject. */
+ * returns -1 for every shape the mask builders reject; 1.6.0 added asa_build_mask_noalloc. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -171,6 +172,34 @@ asa_status asa_build_mask(const void* Q, const void* K, const asa_shape* shape,
                           const asa_adaptive* adaptive, const asa_head_pattern* patterns,
                           const asa_csr* out, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Bytes of the static device scratch array behind asa_build_mask_noalloc (per GPU). */
+#define ASA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * asa_build_mask_noalloc -- asa_build_mask for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Computes exactly what asa_build_mask computes (the same kernels; bit-identical CSR and
+ * order), but takes no workspace argument: the pooled Q and K, row bitmasks and counts live
+ * in a static device array of ASA_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends.  The call allocates nothing and frees
+ * nothing; the first call on a device looks up that device's copy of the array (with the
+ * device current), later calls reuse the address.  It runs on the current device, and
+ * `stream` must belong to it.
+ *
+ * Every argument as asa_build_mask.  Limit: asa_build_mask_workspace_size(shape) must not
+ * exceed ASA_NOALLOC_SCRATCH_BYTES (enough for B*H*Nb*d*16 bytes of pooled Q and K plus
+ * the bitmask: e.g. 24 heads, N = 75600, d = 128 at blk = 128); a larger shape returns
+ * ASA_ERR_WORKSPACE and enqueues nothing.
+ * Concurrency: every call on one GPU shares that GPU's array, and each call overwrites it
+ * entirely before reading it (nothing has to start at zero).  Calls whose work overlaps on
+ * one GPU -- on different streams, or from different threads without ordering -- race on
+ * the array and give undefined masks; order them on one stream.
+ */
+asa_status asa_build_mask_noalloc(const void* Q, const void* K, const asa_shape* shape,
+                                  const asa_adaptive* adaptive, const asa_head_pattern* patterns,
+                                  const asa_csr* out, void* stream);
 
 /*
  * asa_static_mask -- block mask from per-head static patterns alone (Sparse-vDiT mode

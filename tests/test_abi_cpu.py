@@ -101,6 +101,31 @@ def test_build_mask_rejects_arguments():
     assert _build(s, pats=bad) == BAD_PATTERN
 
 
+def test_build_mask_noalloc_rejects_arguments():
+    """The variant without allocation validates like asa_build_mask, and rejects shapes whose
+    workspace exceeds its static scratch before looking the scratch up."""
+    assert asa.lib.asa_build_mask_noalloc.argtypes[-1] is ctypes.c_void_p
+    s = _shape()
+    ad = asa_adaptive(asa.TOPK, 4, 0.0, 0, 0, 1)
+    csr = _csr(asa.lib.asa_csr_capacity(ctypes.byref(s)))
+    call = lambda shape, c=csr, q=FAKE, a=ad: asa.lib.asa_build_mask_noalloc(
+        q, FAKE, ctypes.byref(shape), ctypes.byref(a), None, ctypes.byref(c), None)
+    assert call(s, q=None) == NULL_ARG
+    assert call(_shape(d=96)) == UNSUPPORTED
+    assert call(s, c=_csr(10)) == CAPACITY
+    assert call(s, a=asa_adaptive(asa.TOPK, -1, 0.0, 0, 0, 1)) == BAD_PARAM
+    big = _shape(B=2, H=24, N=75600, d=128, blk=128)
+    need = asa.lib.asa_build_mask_workspace_size(ctypes.byref(big))
+    assert need > asa.NOALLOC_SCRATCH_BYTES
+    assert call(big, c=_csr(asa.lib.asa_csr_capacity(ctypes.byref(big)))) == WORKSPACE
+    assert "static scratch" in asa.lib.asa_last_error().decode()
+    # the five workload shapes fit (the largest is the 720p-like layer, 24 heads)
+    for B, H, N, d in [(1, 2, 1024, 64), (1, 8, 8192, 64), (1, 48, 17776, 64), (1, 12, 32760, 128),
+                       (1, 24, 75600, 128)]:
+        sh = _shape(B=B, H=H, N=N, d=d, blk=128)
+        assert 0 < asa.lib.asa_build_mask_workspace_size(ctypes.byref(sh)) <= asa.NOALLOC_SCRATCH_BYTES
+
+
 def test_static_mask_rejects_arguments():
     s = _shape()
     cap = asa.lib.asa_csr_capacity(ctypes.byref(s))
@@ -281,7 +306,7 @@ def test_plain_c_client_links_and_calls(tmp_path):
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10500
+    assert asa.lib.asa_version() >= 10600
 
 
 def test_invalid_shape_left_to_the_builder():
