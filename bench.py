@@ -58,7 +58,7 @@ def load_traffic(kernel_tag):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, x, budget_s):
+def cpu_baseline(cfg, x, budget_s, mask_heads=None):
     """The float64 oracle on the host cores, on a bounded sample of the same workload."""
     import numpy as np
     import gen
@@ -81,18 +81,32 @@ def cpu_baseline(cfg, x, budget_s):
                     break
     except OSError:
         pass
-    q64, k64, v64 = (gen.as_float64(x[n]) for n in ("q", "k", "v"))
+    heads = list(range(cfg.H)) if mask_heads is None else list(mask_heads)
+    sub = (lambda t: t[:, heads]) if len(heads) < cfg.H else (lambda t: t)
+    q64, k64, v64 = (gen.as_float64(sub(x[n])) for n in ("q", "k", "v"))
+    pats = None if cfg.patterns is None else [cfg.patterns[h] for h in heads]
     t0 = time.perf_counter()
-    M = O.build_mask(q64, k64, cfg.blk, mode=cfg.mode, k=cfg.k, keep_diag=cfg.keep_diag)
+    if cfg.kind == "static":
+        M = O.static_mask(cfg.B, len(heads), cfg.N, cfg.blk, pats)
+    else:
+        M = O.build_mask(q64, k64, cfg.blk, mode=cfg.mode, k=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap,
+                         n_text=cfg.n_text, keep_diag=cfg.keep_diag, patterns=pats)
     t_mask = time.perf_counter() - t0
+    if pats is not None:                  # skipped heads attend nothing
+        for i, (pid, _) in enumerate(pats):
+            if pid == gen.SKIP:
+                M[:, i] = False
     total_flops = O.kept_tile_flops(M, cfg.N, cfg.blk, cfg.d)
+    if total_flops == 0.0:
+        total_flops = 1.0
     # attention on whole query blocks, drawn at random over all heads, until the time
     # budget is spent
     t_att, flops_done, blocks = 0.0, 0.0, 0
     rng = np.random.default_rng(0)
-    order = rng.permutation(cfg.B * cfg.H * cfg.Nb)
+    Hs = len(heads)
+    order = rng.permutation(cfg.B * Hs * cfg.Nb)
     for idx in order:
-        b, rem = divmod(int(idx), cfg.H * cfg.Nb)
+        b, rem = divmod(int(idx), Hs * cfg.Nb)
         h, r = divmod(rem, cfg.Nb)
         t0 = time.perf_counter()
         O.attention_block(q64, k64, v64, M, cfg.blk, b, h, r)
@@ -102,18 +116,96 @@ def cpu_baseline(cfg, x, budget_s):
         blocks += 1
         if t_att + t_mask > budget_s:
             break
-    t_step = t_mask + t_att * total_flops / flops_done
+    # scale the sampled heads up to the whole layer: mask time by heads, attention by flops
+    scale_h = cfg.H / Hs
+    t_step = t_mask * scale_h + (t_att * total_flops / flops_done if flops_done > 0 else 0.0) * scale_h
+    total_flops *= scale_h
+    which = f"all {cfg.H} heads" if Hs == cfg.H else f"heads {heads} of {cfg.H}"
     return {
         "value": total_flops / t_step / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 oracle: full adaptive mask build for all {cfg.H} heads ({t_mask:.2f} s) + "
-                   f"attention on {blocks} of {cfg.B * cfg.H * cfg.Nb} query blocks drawn over all heads ({t_att:.2f} s), "
-                   f"extrapolated by kept-tile flops to one step ({t_step:.1f} s)"),
+        "sample": (f"float64 oracle: {cfg.kind} mask build for {which} ({t_mask:.2f} s) + "
+                   f"attention on {blocks} of {cfg.B * Hs * cfg.Nb} query blocks of those heads ({t_att:.2f} s), "
+                   f"extrapolated by heads and kept-tile flops to one step ({t_step:.1f} s)"),
         "step_seconds_extrapolated": t_step,
         "cpu_model": cpu_model,
         "blas": blas,
     }
 
+
+
+# the other workloads of the layer list: tag -> (config name, oracle mask heads or None for all)
+OTHER_WORKLOADS = [("tiny", "tiny_asa_fp32", None), ("static", "static_patterns_bf16", None),
+                   ("cogvideox", "cogvideox5b_layer", [0, 1]), ("long720p", "long720p_layer", [0, 1])]
+
+
+def bench_workload(tag, cfg, dev, steps, cpu_budget, with_cpu):
+    """Mask build and attention timed on one more workload (HIP events on the launch stream);
+    returns the extra keys of the JSON line, prefixed by `tag`."""
+    import ctypes
+    import numpy as np
+    import torch
+    import block_sparse_attention_asa_amd as asa
+    import gen
+    x = gen.make_inputs(cfg)
+    xd = {k: v.to(dev) for k, v in x.items()}
+    B, H, N, d, blk, Nb = cfg.B, cfg.H, cfg.N, cfg.d, cfg.blk, cfg.Nb
+    rows = B * H * Nb
+    row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(asa.asa_csr_capacity(B, H, N, blk), dtype=torch.int32, device=dev)
+    order = torch.empty(rows, dtype=torch.int32, device=dev)
+    shp = asa.asa_shape(B, H, N, d, blk, asa.ASA_BF16 if cfg.dtype == "bf16" else asa.ASA_F32)
+    static = cfg.kind == "static"
+    wsz = asa.lib.asa_static_mask_workspace_size if static else asa.lib.asa_build_mask_workspace_size
+    ws = torch.empty(int(wsz(ctypes.byref(shp))), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+
+    def build():
+        if static:
+            asa.asa_static_mask(B, H, N, blk, cfg.head_patterns(), dev, out=(row_ptr, col_idx, order), workspace=ws)
+        else:
+            asa.asa_build_mask(xd["q"], xd["k"], blk, cfg.mode, k_top=cfg.k, tau=cfg.tau, k_cap=cfg.k_cap,
+                               n_text=cfg.n_text, keep_diag=cfg.keep_diag, patterns=cfg.patterns,
+                               out=(row_ptr, col_idx, order), workspace=ws)
+
+    def attend():
+        asa.asa_attention_fwd(xd["q"], xd["k"], xd["v"], row_ptr, col_idx, blk, patterns=cfg.patterns,
+                              order=order, out=out)
+
+    for _ in range(3):
+        build()
+        attend()
+    torch.cuda.synchronize()
+    rp_h = row_ptr.cpu().numpy()
+    kept = int(rp_h[-1])
+    flops = kept_tile_flops(rp_h, col_idx[:kept].cpu().numpy(), N, blk, d, H, B)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        build()
+        ev[i][1].record(stream)
+        attend()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    mask_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]))
+    attn_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]))
+    esize = 2 if cfg.dtype == "bf16" else 4
+    mask_bytes = 4.0 * (2 * rows + 1 + kept) + (0.0 if static else 2.0 * B * H * N * d * esize)
+    tfl = flops / attn_ms / 1e9
+    res = {f"{tag}_workload": f"{cfg.name}: B={B} H={H} N={N} d={d} blk={blk} {cfg.dtype}",
+           f"{tag}_kept_tiles": kept, f"{tag}_density": round(kept / (rows * Nb), 5),
+           f"{tag}_attn_ms": round(attn_ms, 4), f"{tag}_attn_tflops": round(tfl, 2),
+           f"{tag}_attn_frac": round(tfl / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
+           f"{tag}_mask_ms": round(mask_ms, 4), f"{tag}_mask_gbs": round(mask_bytes / mask_ms / 1e6, 1)}
+    del xd, row_ptr, col_idx, order, ws, out
+    torch.cuda.empty_cache()
+    if with_cpu:
+        heads = dict((t, h) for t, _, h in OTHER_WORKLOADS)[tag]
+        cb = cpu_baseline(cfg, x, cpu_budget, mask_heads=heads)
+        cb["vs_gpu_step"] = round(cb["step_seconds_extrapolated"] * 1e3 / (mask_ms + attn_ms), 1)
+        res[f"{tag}_cpu_baseline"] = cb
+    return res
 
 def main():
     ap = argparse.ArgumentParser()
@@ -127,6 +219,8 @@ def main():
     ap.add_argument("--no-search", action="store_true", help="skip the per-head pattern search timing")
     ap.add_argument("--no-split", action="store_true", help="skip the split-row timing (one head in full)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the step")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other four workloads (tiny, static, CogVideoX-shaped, 720p-like)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run one device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -361,8 +455,13 @@ def main():
         result_extra["split_case"] = f"one head in full: B={B} H=1 N={N} d={d} blk={blk}, automatic split"
         del h1, frp, fci, fo, fws
 
+    if not args.no_workloads:
+        for tag, name, _ in OTHER_WORKLOADS:
+            log(f"bench: workload {name}")
+            result_extra.update(bench_workload(tag, gen.BY_NAME[name], dev, 10, 3.0, not args.no_cpu_baseline))
+
     attn_tflops = flops / attn_ms / 1e9
-    mask_bytes = 2.0 * B * H * N * d * 2 + 4.0 * (rows + 1 + kept)   # Q, K read once; CSR written
+    mask_bytes = 2.0 * B * H * N * d * 2 + 4.0 * (2 * rows + 1 + kept)   # Q, K read; CSR and order written
     traffic = load_traffic("attn_fwd_wan")
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),

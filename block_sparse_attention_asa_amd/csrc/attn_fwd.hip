@@ -58,8 +58,12 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
   constexpr int kOut = D / 32;     // 32-column output subtiles
   constexpr bool kBf16 = sizeof(T) == 2;
   // The running max is only moved when a row's max grows by more than this (log2 units):
-  // weights are then at most 2^8, exact up to rounding, and the O / l rescale is skipped.
-  constexpr float kRescaleSlack = 8.0f;
+  // weights are then at most 2^32, exact up to rounding, and the O / l rescale is skipped.
+  // The scores of a row span tens of log2 units on video attention, so a small slack
+  // rescales often (about one step in six at 2^8, one in twenty-five at 2^32 on the Wan
+  // layer).  The fp32 accumulator stays finite while 2^32 x max|V| x (kept keys) does,
+  // i.e. for |V| below 2^79.
+  constexpr float kRescaleSlack = 32.0f;
   static_assert(NGS % NT == 0, "tile must split evenly over the workgroup");
   static_assert(GPR >= 8, "swizzle needs at least 8 granules per row");
   static_assert(BLK % KT == 0, "block must be a whole number of steps");

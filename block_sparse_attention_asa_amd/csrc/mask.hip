@@ -18,9 +18,9 @@
 //                    registers, prefix selection and the union with forced / static
 //                    blocks -> bitmask and count.
 //   static_kernel    one wavefront per row: static pattern bitmask only.
-//   csr_scan_kernel  exclusive scan of per-row counts -> row_ptr; optionally the
-//                    processing order (long rows first inside each XCD range).
-//   csr_fill_kernel  one wavefront per row: bitmask -> ascending col_idx.
+//   csr_kernel       per-row counts -> row_ptr (each workgroup sums the counts before its
+//                    rows), bitmask -> ascending col_idx; optionally the processing order
+//                    (long rows first inside each XCD range) from eight more workgroups.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -530,73 +530,69 @@ __global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__
 }
 
 // ------------------------------------------------------------------ CSR
-constexpr int kScanThreads = kOrderThreads;   // the scan launch also builds the order
+// One launch builds the whole CSR (and, when asked, the processing order).  Workgroups
+// 0 .. nfill-1 own kFillRows consecutive rows each: the row offset of their first row is
+// the sum of every earlier row's count (all threads read a strided share, then a
+// workgroup sum in a fixed order), a scan of their own counts gives row_ptr, and each
+// wavefront then turns kFillRows / 16 rows' bitmasks into ascending block indices.
+// Workgroups nfill .. nfill+7 build the order of one XCD range each.
+constexpr int kCsrThreads = kOrderThreads;
+constexpr int kFillRows = 64;
+constexpr int kFillWaves = kCsrThreads / 64;
+constexpr int kRowsPerFillWave = kFillRows / kFillWaves;
 
-// Workgroup 0: row_ptr[0] = 0, row_ptr[i+1] = sum of count[0..i].  Each thread owns a
-// run of consecutive rows; one wave-level scan of the per-thread totals.
-__global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* __restrict__ count,
-                                                                int32_t* __restrict__ row_ptr,
-                                                                int32_t* __restrict__ order,
-                                                                int rows) {
-  __shared__ int wsum[kScanThreads / 64];
+__global__ __launch_bounds__(kCsrThreads) void csr_kernel(const uint32_t* __restrict__ bits,
+                                                          const int32_t* __restrict__ count,
+                                                          int32_t* __restrict__ row_ptr,
+                                                          int32_t* __restrict__ col_idx,
+                                                          int32_t* __restrict__ order, int words,
+                                                          int rows) {
   __shared__ OrderScratch osh;
-  if (blockIdx.x > 0) {   // workgroups 1..8: the processing order of one XCD range each
-    order_range([&](int i) { return count[i]; }, order, rows, blockIdx.x - 1, osh);
+  __shared__ int wsum[kFillWaves];
+  __shared__ int start[kFillRows];
+  const int nfill = (rows + kFillRows - 1) / kFillRows;
+  if ((int)blockIdx.x >= nfill) {
+    order_range([&](int i) { return count[i]; }, order, rows, (int)blockIdx.x - nfill, osh);
     return;
   }
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int per = (rows + kScanThreads - 1) / kScanThreads;
-  const int t0 = threadIdx.x * per;
-  int local = 0;
-  for (int i = 0; i < per; ++i)
-    if (t0 + i < rows) local += count[t0 + i];
-  int incl = local;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
-  if (lane == 63) wsum[wv] = incl;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int row0 = (int)blockIdx.x * kFillRows;
+  // offset of row0: counts of rows 0 .. row0-1
+  int part = 0;
+  for (int i = tid; i < row0; i += kCsrThreads) part += count[i];
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+  if (lane == 0) wsum[wv] = part;
   __syncthreads();
   if (wv == 0) {
-    const int v0 = lane < kScanThreads / 64 ? wsum[lane] : 0;
-    int x = v0;
+    int base = 0;
+    for (int w = 0; w < kFillWaves; ++w) base += wsum[w];
+    const int cnt = row0 + lane < rows ? count[row0 + lane] : 0;   // kFillRows == 64 lanes
+    int incl = cnt;
     for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(x, off, 64);
-      if (lane >= off) x += v;
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
     }
-    if (lane < kScanThreads / 64) wsum[lane] = x - v0;   // exclusive
+    start[lane] = base + incl - cnt;
+    if (row0 + lane < rows) row_ptr[row0 + lane + 1] = base + incl;
+    if (row0 == 0 && lane == 0) row_ptr[0] = 0;
   }
   __syncthreads();
-  int run = wsum[wv] + incl - local;
-  if (threadIdx.x == 0) row_ptr[0] = 0;
-  for (int i = 0; i < per; ++i) {
-    if (t0 + i < rows) {
-      run += count[t0 + i];
-      row_ptr[t0 + i + 1] = run;
+  for (int k = 0; k < kRowsPerFillWave; ++k) {
+    const int rr = wv * kRowsPerFillWave + k, row = row0 + rr;
+    if (row >= rows) break;
+    uint32_t w = lane < words ? bits[(size_t)row * words + lane] : 0u;
+    const int pc = __popc(w);
+    int incl = pc;   // inclusive prefix over lanes
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
     }
-  }
-}
-
-// One wavefront per row: kept bits -> ascending block indices.
-__global__ __launch_bounds__(kThreads) void csr_fill_kernel(const uint32_t* __restrict__ bits,
-                                                            const int32_t* __restrict__ row_ptr,
-                                                            int32_t* __restrict__ col_idx,
-                                                            int words, int rows) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  uint32_t w = lane < words ? bits[(size_t)row * words + lane] : 0u;
-  const int pc = __popc(w);
-  int incl = pc;   // inclusive prefix over lanes
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
-  int out = row_ptr[row] + incl - pc;
-  while (w) {
-    const int b = __ffs(w) - 1;
-    col_idx[out++] = lane * 32 + b;
-    w &= w - 1u;
+    int out = start[rr] + incl - pc;
+    while (w) {
+      const int b = __ffs(w) - 1;
+      col_idx[out++] = lane * 32 + b;
+      w &= w - 1u;
+    }
   }
 }
 
@@ -675,13 +671,9 @@ hipError_t launch_static_rows(const MaskGeom& g, const HeadTable& heads, const M
 hipError_t launch_csr(const MaskGeom& g, const MaskWorkspace& ws, int32_t* row_ptr,
                       int32_t* col_idx, int32_t* order, hipStream_t s) {
   const int rows = g.B * g.H * g.Nb;
-  // workgroup 0 scans the counts; with an order, workgroups 1..8 order one XCD range each
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(order ? 1 + kXcds : 1), dim3(kScanThreads), 0, s, ws.count,
-                     row_ptr, order, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0, s, ws.bits,
-                     row_ptr, col_idx, g.words, rows);
+  const int nfill = (rows + kFillRows - 1) / kFillRows;
+  hipLaunchKernelGGL(csr_kernel, dim3((unsigned)(nfill + (order ? kXcds : 0))), dim3(kCsrThreads), 0, s, ws.bits,
+                     ws.count, row_ptr, col_idx, order, g.words, rows);
   return hipGetLastError();
 }
 
