@@ -68,13 +68,10 @@ __device__ inline double bf16_to_f64(uint16_t x) {
 }
 
 // ------------------------------------------------------------------ static patterns
-__device__ inline long long floor_div(long long a, long long b) {  // b > 0
-  long long q = a / b;
-  if ((a % b != 0) && (a < 0)) --q;
-  return q;
-}
-
-// Is key block c kept in query-block row r by static pattern (id, param)?
+// Is key block c kept in query-block row r by static pattern (id, param)?  Everything is
+// 32-bit: token indices lie in [0, N) and their differences in (-N, N), with N an int, and
+// the divisions are by a per-head constant (64-bit integer division is a long emulated
+// sequence on the GPU).
 __device__ inline bool static_keep(int id, int param, int r, int c, int N, int blk, int Nb) {
   switch (id) {
     case 1:  // full
@@ -84,20 +81,18 @@ __device__ inline bool static_keep(int id, int param, int r, int c, int N, int b
     case 5:  // vertical stripe: leading `param` key blocks
       return c < param;
     case 4: {  // multi-diagonal, stride `param` tokens
-      const long long qlo = (long long)r * blk;
-      const long long qhi = min(qlo + blk, (long long)N) - 1;
-      const long long klo = (long long)c * blk;
-      const long long khi = min(klo + blk, (long long)N) - 1;
-      const long long lo = klo - qhi, hi = khi - qlo;   // range of j - i over the tile
-      const long long S = param;
-      return floor_div(hi, S) * S >= lo;                // a multiple of S lies in [lo, hi]
+      const int qlo = r * blk, qhi = qlo + min(blk, N - qlo) - 1;
+      const int klo = c * blk, khi = klo + min(blk, N - klo) - 1;
+      const int lo = klo - qhi, width = (khi - qlo) - lo;   // j - i spans [lo, lo + width]
+      // the first multiple of S at or above lo is lo + (S - lo mod S) unless S divides lo
+      int m = lo % param;
+      if (m < 0) m += param;
+      return m == 0 || width >= param - m;
     }
     case 6: {  // frame tiles of `param` tokens: the query's own frames and frame 0
-      const long long F = param;
-      const long long qlo = (long long)r * blk;
-      const long long qhi = min(qlo + blk, (long long)N) - 1;
-      const long long klo = (long long)c * blk;
-      const long long khi = min(klo + blk, (long long)N) - 1;
+      const unsigned F = (unsigned)param;
+      const unsigned qlo = (unsigned)(r * blk), qhi = qlo + (unsigned)min(blk, N - (int)qlo) - 1u;
+      const unsigned klo = (unsigned)(c * blk), khi = klo + (unsigned)min(blk, N - (int)klo) - 1u;
       if (klo < F) return true;                         // the block holds frame-0 keys
       return klo / F <= qhi / F && qlo / F <= khi / F;  // frame ranges overlap
     }
@@ -180,11 +175,15 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 // Scores: S = Qp KpT / sqrt(d) for those rows against all Nb key blocks, a dense float64
 // contraction on the fp64 matrix cores (v_mfma_f64_16x16x4f64), written to LDS.  Operand
 // layout of the instruction, per lane l: A holds row l%16, k = l/16; B holds k = l/16,
-// column l%16; result component e holds row 4e + l/16, column l%16.  The A operand (the
-// rows' pooled queries, copied once into LDS with 16-byte loads) stays in registers while
-// the wavefronts take 16-column tiles in turn, with two accumulators on alternate k-steps.
+// column l%16; result component e holds row 4e + l/16, column l%16.  The rows' pooled
+// queries are copied once into LDS with 16-byte loads; the wavefronts take 16-column tiles
+// in turn, with two accumulators on alternate k-steps.  The workgroup size depends on d:
+// at d = 128 the contraction streams twice the KpT bytes per tile, and sixteen wavefronts
+// (four per SIMD, one row each, the A operand read from LDS at each k-step) hide that
+// latency best; at d = 64 eight wavefronts keep the whole A operand in registers and take
+// two rows each, which lets the mass-prefix path sort two rows side by side.
 //
-// Selection: each of the eight wavefronts ranks kRankRowsPerWave rows.  Rank order is value
+// Selection: each wavefront ranks rows_per_wave rows.  Rank order is value
 // descending, then block index ascending, and a key packs both into one uint64: the
 // value's bits made order-preserving as an unsigned integer, its lowest 10 bits replaced
 // by 1023 - c.  Dropping those bits merges values closer than 2^-42 relative (far inside
@@ -196,9 +195,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 // inside a lane's registers and the others cross lanes at distance J / PER; RI rows go
 // through the network side by side for instruction-level parallelism.
 constexpr int kRankRows = 16;
-constexpr int kRankThreads = 512;   // two wavefronts per SIMD
-constexpr int kRankWaves = kRankThreads / 64;
-constexpr int kRankRowsPerWave = kRankRows / kRankWaves;
+constexpr int rank_threads(int d) { return d >= 128 ? 1024 : 512; }
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
 __device__ inline uint64_t rank_key(double v, int c) {
@@ -321,13 +318,16 @@ __device__ inline uint64_t select_kth(const uint64_t (&kv)[PER], const uint64_t 
 // The ids an XCD receives map onto one contiguous range of row tiles, so the tiles of a
 // head (which all read that head's KpT) share an L2.
 template <int D, int NP2>
-__global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __restrict__ qp,
+__global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __restrict__ qp,
                                                         const double* __restrict__ kpt,
                                                         uint32_t* __restrict__ bits,
                                                         int32_t* __restrict__ count, MaskGeom g,
                                                         AdaptiveParams p, HeadTable heads) {
+  constexpr int kRankThreads = rank_threads(D);
+  constexpr int kRankWaves = kRankThreads / 64;
+  constexpr int kRankRowsPerWave = kRankRows / kRankWaves;
   constexpr int PER = NP2 / 64;
-  constexpr int RI = PER >= 16 ? 1 : 2;
+  constexpr int RI = (PER >= 16 || kRankRowsPerWave < 2) ? 1 : 2;
   static_assert(kRankRowsPerWave % RI == 0, "rows per wavefront split into equal passes");
   __shared__ double srow[kRankRows][NP2];
   __shared__ uint32_t word[kRankRows][kMaxMaskBlocks / 32];
@@ -366,21 +366,40 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __rest
     }
     __syncthreads();
     const int kl = lane >> 4;
-    double a[D / 4], b[D / 4];
+    double a[kRankWaves > 8 ? 1 : D / 4];
+    if constexpr (kRankWaves <= 8) {
 #pragma unroll
-    for (int s = 0; s < D / 4; ++s) a[s] = qtile[lane & 15][4 * s + kl];
+      for (int s = 0; s < D / 4; ++s) a[s] = qtile[lane & 15][4 * s + kl];
+    }
     const double sqrt_d = sqrt((double)D);
     const int ctiles = (Nb + 15) / 16;
     for (int ct = w; ct < ctiles; ct += kRankWaves) {
       const int c = ct * 16 + (lane & 15);
       const int cc = min(c, Nb - 1);
-#pragma unroll
-      for (int s = 0; s < D / 4; ++s) b[s] = kt[(size_t)(4 * s + kl) * Nb + cc];
       f64x4_t acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+      if constexpr (kRankWaves > 8) {
+        // A from LDS at each k-step, B streamed from KpT eight k-steps at a time
+#pragma unroll 1
+        for (int s0 = 0; s0 < D / 4; s0 += 8) {
+          double b[8];
 #pragma unroll
-      for (int s = 0; s < D / 4; s += 2) {
-        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], b[s + 1], acc1, 0, 0, 0);
+          for (int j = 0; j < 8; ++j) b[j] = kt[(size_t)(4 * (s0 + j) + kl) * Nb + cc];
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qtile[lane & 15][4 * (s0 + j) + kl], b[j], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qtile[lane & 15][4 * (s0 + j + 1) + kl], b[j + 1], acc1, 0, 0, 0);
+          }
+        }
+      } else {
+        // A held in registers across tiles, all of B loaded before the first product
+        double b[D / 4];
+#pragma unroll
+        for (int s = 0; s < D / 4; ++s) b[s] = kt[(size_t)(4 * s + kl) * Nb + cc];
+#pragma unroll
+        for (int s = 0; s < D / 4; s += 2) {
+          acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s], b[s], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s + 1], b[s + 1], acc1, 0, 0, 0);
+        }
       }
       if (c < Nb) {
 #pragma unroll
@@ -507,7 +526,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(const double* __rest
 }
 
 // ------------------------------------------------------------------ static-only rows
-// One wavefront per row, 4 rows per workgroup.
+// One wavefront per row, 4 rows per workgroup; each pass tests 64 key blocks, one per lane,
+// and a ballot gives two 32-bit words of the row.
 __global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__ bits,
                                                           int32_t* __restrict__ count,
                                                           MaskGeom g, HeadTable heads, int rows) {
@@ -516,16 +536,15 @@ __global__ __launch_bounds__(kThreads) void static_kernel(uint32_t* __restrict__
   if (row >= rows) return;
   const int bh = row / g.Nb, r = row - bh * g.Nb, h = bh % g.H;
   const int pid = heads.id[h], prm = heads.param[h];
-  uint32_t w = 0u;
-  if (lane < g.words) {
-    for (int b = 0; b < 32; ++b) {
-      const int c = lane * 32 + b;
-      if (c < g.Nb && static_keep(pid, prm, r, c, g.N, g.blk, g.Nb)) w |= 1u << b;
-    }
-    bits[(size_t)row * g.words + lane] = w;
+  uint32_t* out = bits + (size_t)row * g.words;
+  int pc = 0;
+  for (int c0 = 0; c0 < g.Nb; c0 += 64) {
+    const int c = c0 + lane;
+    const uint64_t m = __ballot(c < g.Nb && static_keep(pid, prm, r, c, g.N, g.blk, g.Nb));
+    const int wi = (c0 >> 5) + lane;
+    if (lane < 2 && wi < g.words) out[wi] = (uint32_t)(lane ? m >> 32 : m);
+    pc += __popcll(m);
   }
-  int pc = __popc(w);
-  for (int off = 32; off > 0; off >>= 1) pc += __shfl_xor(pc, off, 64);
   if (lane == 0) count[row] = pc;
 }
 
@@ -642,7 +661,7 @@ template <int D>
 static hipError_t launch_rank_d(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
                                 const MaskWorkspace& ws, hipStream_t s) {
   const int tiles = (g.Nb + kRankRows - 1) / kRankRows;
-  const dim3 grid((unsigned)(g.B * g.H * tiles)), block(kRankThreads);
+  const dim3 grid((unsigned)(g.B * g.H * tiles)), block(rank_threads(D));
   int np2 = 64;
   while (np2 < g.Nb) np2 <<= 1;
   switch (np2) {
