@@ -198,6 +198,29 @@ def bench_workload(tag, cfg, dev, steps, cpu_budget, with_cpu):
            f"{tag}_attn_ms": round(attn_ms, 4), f"{tag}_attn_tflops": round(tfl, 2),
            f"{tag}_attn_frac": round(tfl / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
            f"{tag}_mask_ms": round(mask_ms, 4), f"{tag}_mask_gbs": round(mask_bytes / mask_ms / 1e6, 1)}
+    if static:
+        # One full head among diagonal and stripe heads: its rows hold most of the kept
+        # tiles, so the launch waits on a few long rows.  Split rows (16 blocks a chunk)
+        # spread them over the chip; same mask, same output up to the merge's rounding.
+        sws = torch.empty(max(1, int(asa.lib.asa_attention_fwd_split_workspace_size(ctypes.byref(shp), 16))),
+                          dtype=torch.uint8, device=dev)
+
+        def attend_split():
+            asa.asa_attention_fwd_split(xd["q"], xd["k"], xd["v"], row_ptr, col_idx, blk, split_blocks=16,
+                                        patterns=cfg.patterns, order=order, out=out, workspace=sws)
+
+        for _ in range(3):
+            attend_split()
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        sev[0].record(stream)
+        for _ in range(steps):
+            attend_split()
+        sev[1].record(stream)
+        torch.cuda.synchronize()
+        split_ms = sev[0].elapsed_time(sev[1]) / steps
+        res[f"{tag}_split16_attn_ms"] = round(split_ms, 4)
+        res[f"{tag}_split16_attn_tflops"] = round(flops / split_ms / 1e9, 2)
+        del sws
     del xd, row_ptr, col_idx, order, ws, out
     torch.cuda.empty_cache()
     if with_cpu:
