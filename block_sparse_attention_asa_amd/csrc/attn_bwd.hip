@@ -15,7 +15,8 @@
 //   bwd_prep_kernel  per query: (lse * log2 e, D = dO . O) -> workspace pairs.
 //   csc_kernel       one workgroup per head: CSR -> CSC (key block -> query blocks in
 //                    ascending order) through a transposed bitmask in LDS.
-//   col_order_kernel the key-block schedule: longest lists first inside each XCD range.
+//   col_order_kernel the key-block schedule: an equal share of every list-length class per
+//                    XCD, longest lists first.
 //   dq_kernel        one workgroup per query-block row, like the forward (and in the CSR's
 //                    processing order when there is one): K and V of every
 //                    kept key block stream through an LDS ring; per 64-key step
@@ -141,15 +142,16 @@ __global__ __launch_bounds__(kCscThreads) void csc_kernel(const int32_t* __restr
   if (bh == heads - 1 && tid == 0) col_ptr[heads * Nb] = row_ptr[heads * Nb];
 }
 
-// Key-block schedule for dkv_kernel: inside each XCD range, key blocks by descending length
-// class of their query-block lists (skipped heads count as empty), so the blocks kept by
-// many query blocks start first.  One workgroup per XCD range.
+// Key-block schedule for dkv_kernel (order_balanced over the lengths of the key blocks'
+// query-block lists; skipped heads count as empty): every XCD gets an equal share of each
+// length class, and the blocks kept by many query blocks start first.  One workgroup per
+// XCD range.
 __global__ __launch_bounds__(kOrderThreads) void col_order_kernel(const int32_t* __restrict__ col_ptr,
                                                                   int32_t* __restrict__ col_order,
                                                                   int Nb, int H, int total,
                                                                   SkipBits skip) {
   __shared__ OrderScratch sh;
-  order_range(
+  order_balanced(
       [&](int i) {
         const int h = (i / Nb) % H;
         return ((skip.bits[h >> 5] >> (h & 31)) & 1u) ? 0 : col_ptr[i + 1] - col_ptr[i];

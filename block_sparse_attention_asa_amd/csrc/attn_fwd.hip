@@ -72,8 +72,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
   __shared__ uint4 Vt[2][NGS];
 
   // work item -> position in the processing order (and, with split rows, the chunk of the
-  // row).  Positions map to rows through a permutation from the mask builder, which lists
-  // long rows first inside each XCD's range, or the identity.
+  // row).  Positions map to rows through a permutation from the mask builder, which gives
+  // every XCD an equal share of each row-length class, long rows first, or the identity.
   int pos, chunk = 0;
   if constexpr (kSplit) {
     // each XCD walks its own range of rows, all chunks of a row together; the grid is

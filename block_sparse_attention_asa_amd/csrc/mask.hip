@@ -20,7 +20,8 @@
 //   static_kernel    one wavefront per row: static pattern bitmask only.
 //   csr_kernel       per-row counts -> row_ptr (each workgroup sums the counts before its
 //                    rows), bitmask -> ascending col_idx; optionally the processing order
-//                    (long rows first inside each XCD range) from eight more workgroups.
+//                    (an equal share of every row-length class per XCD, long rows first)
+//                    from eight more workgroups.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(const uint32_t* __rest
   __shared__ int start[kFillRows];
   const int nfill = (rows + kFillRows - 1) / kFillRows;
   if ((int)blockIdx.x >= nfill) {
-    order_range([&](int i) { return count[i]; }, order, rows, (int)blockIdx.x - nfill, osh);
+    order_balanced([&](int i) { return count[i]; }, order, rows, (int)blockIdx.x - nfill, osh);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;

@@ -104,16 +104,23 @@ typedef struct asa_head_pattern {
  *
  * order (optional, may be NULL) is the attention schedule: a device int32 array of
  * B*H*Nb entries holding a permutation of the rows.  The pages leave the work order open;
- * this schedule exists for load balance.  It splits the rows into 8 contiguous ranges,
- * one per XCD of the MI355X (range x starts at
- * x*floor(R/8) + min(x, R%8) for R rows, and the first R%8 ranges hold one extra row).
- *   - asa_build_mask / asa_static_mask fill it when non-NULL.  Inside each range the rows
- *     come longest first: by length class (0 for an empty row, else 1 + floor(log2 of
- *     the kept count)) descending, ties in row order.  The result is deterministic.
+ * this schedule exists for load balance.  Its positions split into 8 contiguous ranges,
+ * one per XCD of the MI355X (range x starts at x*floor(R/8) + min(x, R%8) for R rows, and
+ * the first R%8 ranges hold one extra position); the rows at the positions of range x run
+ * on XCD x.
+ *   - asa_build_mask / asa_static_mask fill it when non-NULL, as follows.  A row's length
+ *     class is 0 when it is empty, else 1 + floor(log2 of its kept count).  The rows of each
+ *     class, in row order, are cut into 8 consecutive slices; range x holds slice x of every
+ *     class, longest class first, each slice in row order.  Class c (s_c rows) has slices
+ *     of floor(s_c/8) rows, and s_c%8 of them one row more: those go to the XCDs
+ *     cursor, cursor+1, ... (mod 8), where cursor starts at 0 for the longest class and
+ *     advances by s_c%8 (mod 8) after each class.  So every XCD gets an equal share of the
+ *     long rows, a slice is a run of neighbouring rows, and each range has exactly its
+ *     number of positions.  The result is deterministic.
  *   - asa_attention_fwd processes the rows in this order when it is non-NULL, and in row
  *     order otherwise.  The outputs are bit-identical either way.  A caller-made order
- *     must be a permutation of 0..B*H*Nb-1 that keeps every row inside its range, or rows
- *     go unwritten (not checked: the array is device memory). */
+ *     must be a permutation of 0..B*H*Nb-1, or rows go unwritten (not checked: the array
+ *     is device memory). */
 typedef struct asa_csr {
   int32_t* row_ptr;
   int32_t* col_idx;
@@ -124,7 +131,8 @@ typedef struct asa_csr {
 /* Library version (major*10000 + minor*100 + patch).  1.1.0 added asa_csr.order;
  * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split; 1.4.0 added
  * ASA_PAT_FRAME_TILE; 1.5.0: asa_attention_bwd follows asa_csr.order, and asa_csr_capacity
- * returns -1 for every shape the mask builders reject; 1.6.0 added asa_build_mask_noalloc. */
+ * returns -1 for every shape the mask builders reject; 1.6.0 added asa_build_mask_noalloc;
+ * 1.7.0: the schedule gives every XCD an equal share of each row-length class. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */

@@ -306,7 +306,7 @@ def test_plain_c_client_links_and_calls(tmp_path):
 def test_status_strings():
     assert asa.lib.asa_status_string(0) == b"ASA_OK"
     assert asa.lib.asa_status_string(-5) == b"ASA_ERR_CAPACITY"
-    assert asa.lib.asa_version() >= 10600
+    assert asa.lib.asa_version() >= 10700
 
 
 def test_invalid_shape_left_to_the_builder():

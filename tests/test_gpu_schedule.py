@@ -1,11 +1,14 @@
 """GPU: the attention schedule (asa_csr.order) that the mask builders emit.
 
-The pages leave the work order open; the rule here is the one stated in asa.h.  Rows
-split into 8 contiguous ranges, one per XCD.  Inside each range they come by length
-class (0 for an empty row, else 1 + floor(log2 of the kept count)) descending, ties in
-row order.  The test re-derives that rule on the host from the builder's own row_ptr and
-requires the device order to match it exactly.  Attention must give bit-identical
-outputs with and without the order: it changes when rows run, not what they compute.
+The pages leave the work order open; the rule here is the one stated in asa.h.  Positions
+split into 8 contiguous ranges, one per XCD.  Rows group by length class (0 for an empty
+row, else 1 + floor(log2 of the kept count)); each class, in row order, is cut into 8
+consecutive slices, and range x holds slice x of every class, longest class first.  The
+s_c mod 8 one-row-larger slices of a class go to the XCDs from a cursor that starts at 0
+and advances by s_c mod 8 after each class.  The test re-derives that rule on the host
+from the builder's own row_ptr and requires the device order to match it exactly.
+Attention must give bit-identical outputs with and without the order: it changes when
+rows run, not what they compute.
 """
 import numpy as np
 import pytest
@@ -23,13 +26,23 @@ def expected_order(row_ptr: np.ndarray) -> np.ndarray:
     counts = np.diff(row_ptr.astype(np.int64))
     rows = counts.size
     per, rem = divmod(rows, N_XCD)
-    out = np.empty(rows, dtype=np.int64)
-    for x in range(N_XCD):
-        lo = x * per + min(x, rem)
-        hi = lo + per + (1 if x < rem else 0)
-        idx = np.arange(lo, hi)
-        cls = np.array([int(c).bit_length() for c in counts[lo:hi]], dtype=np.int64)
-        out[lo:hi] = idx[np.lexsort((idx, -cls))]
+    lo = [x * per + min(x, rem) for x in range(N_XCD)]
+    hi = [lo[x] + per + (1 if x < rem else 0) for x in range(N_XCD)]
+    cls = np.array([int(c).bit_length() for c in counts], dtype=np.int64)
+    out = np.full(rows, -1, dtype=np.int64)
+    fill = list(lo)
+    cursor = 0
+    for c in range(int(cls.max()) if rows else 0, -1, -1):
+        members = np.nonzero(cls == c)[0]          # ascending row index
+        b, e = divmod(members.size, N_XCD)
+        taken = 0
+        for x in range(N_XCD):
+            size = b + (1 if (x - cursor) % N_XCD < e else 0)
+            out[fill[x]:fill[x] + size] = members[taken:taken + size]
+            fill[x] += size
+            taken += size
+        cursor = (cursor + e) % N_XCD
+    assert fill == hi
     return out
 
 
