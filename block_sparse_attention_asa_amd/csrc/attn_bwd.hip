@@ -345,13 +345,23 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int is = 0; is < kSub; ++is) {
         f32x16_t s = f32x16_t{}, dp = f32x16_t{};
         const int kr = 32 * is + qn;
-#pragma unroll
-        for (int t = 0; t < kQk; ++t) {
-          Frag<T> ka, va;
+        // the K and V fragments of k-step t+2 are read before the products of k-step t
+        // (an order fixed with scheduling fences)
+        auto kv_frag = [&](int t, Frag<T>& ka, Frag<T>& va) {
           ka.v = kt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
           va.v = vt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
-          mma_k16(s, ka, qf[t]);
-          mma_k16(dp, va, df[t]);
+        };
+        Frag<T> ka[3], va[3];
+        kv_frag(0, ka[0], va[0]);
+        kv_frag(1, ka[1], va[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < kQk; ++t) {
+          if (t + 2 < kQk) kv_frag(t + 2, ka[(t + 2) % 3], va[(t + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_k16(s, ka[t % 3], qf[t]);
+          mma_k16(dp, va[t % 3], df[t]);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -364,22 +374,35 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
           }
           dsf[2 * is + h2] = pack_bf16(x);
           if (nv < KT) {   // keys past N (the last, partial key block only): P = 0, so dS = +-0
+            // element 2j is key 32is + 8(2h2 + j/2) + 4hf + 2(j%2), compared as a constant
+            // against nv - 4hf so that no key index stays live across the loop
+            const int nvh = nv - 4 * hf;
             uint32_t drop[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int key = 32 * is + 8 * (2 * h2 + (j >> 1)) + 4 * hf + 2 * (j & 1);   // element 2j
-              drop[j] = (key >= nv ? 0x0000FFFFu : 0u) | (key + 1 >= nv ? 0xFFFF0000u : 0u);
+              const int key = 32 * is + 8 * (2 * h2 + (j >> 1)) + 2 * (j & 1);
+              drop[j] = (key >= nvh ? 0x0000FFFFu : 0u) | (key + 1 >= nvh ? 0xFFFF0000u : 0u);
             }
             clear_bf16(dsf[2 * is + h2], drop, true);
           }
         }
       }
-      // dQ^T += K^T dS^T (K^T fragments by transpose reads of the K tile)
+      // dQ^T += K^T dS^T (K^T fragments by transpose reads of the K tile, the next pair's
+      // read before the current pair's product)
       const uint16_t* ktile = reinterpret_cast<const uint16_t*>(kt);
+      {
+        constexpr int kPairs = kOut * kPv;
+        Frag<T> tk[2];
+        tk[0] = tr_frag<D>(ktile, 0, 0, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int io = 0; io < kOut; ++io)
-#pragma unroll
-        for (int u = 0; u < kPv; ++u) mma_k16(acc[io], tr_frag<D>(ktile, io, u, lane), dsf[u]);
+        for (int pp = 0; pp < kPairs; ++pp) {
+          if (pp + 1 < kPairs) tk[(pp + 1) % 2] = tr_frag<D>(ktile, (pp + 1) / kPv, (pp + 1) % kPv, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_k16(acc[pp / kPv], tk[pp % 2], dsf[pp % kPv]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
 
       if (!more) break;
       e = e_n;
@@ -535,11 +558,13 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
         pf[u] = pack_bf16(pv);
         dsf[u] = pack_bf16(dsv);
         if (nq < QT) {   // queries past N (the last, partial query block only): P = 0, dS = +-0
+          // element 2j is query 16u + 8(j/2) + 4hf + 2(j%2), compared against nq - 4hf
+          const int nqh = nq - 4 * hf;
           uint32_t drop[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int q = 16 * u + 8 * (j >> 1) + 4 * hf + 2 * (j & 1);   // element 2j
-            drop[j] = (q >= nq ? 0x0000FFFFu : 0u) | (q + 1 >= nq ? 0xFFFF0000u : 0u);
+            const int q = 16 * u + 8 * (j >> 1) + 2 * (j & 1);
+            drop[j] = (q >= nqh ? 0x0000FFFFu : 0u) | (q + 1 >= nqh ? 0xFFFF0000u : 0u);
           }
           clear_bf16(pf[u], drop, false);
           clear_bf16(dsf[u], drop, true);

@@ -191,14 +191,14 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
         const uint4* kt = Kt[kSlot];
         const T* vt = reinterpret_cast<const T*>(Vt[kSlot]);
 
-        // S^T = K Q^T
+        // S^T = K Q^T; the K fragment of k-step t+3 is read before the product of k-step t
+        // (fixed with scheduling fences, as for the V^T fragments below)
         f32x16_t s[kSub];
   #pragma unroll
         for (int is = 0; is < kSub; ++is) {
           s[is] = f32x16_t{};
           const int kr = 32 * is + qn;
-  #pragma unroll
-          for (int t = 0; t < kQk; ++t) {
+          auto kfrag = [&](int t) {
             Frag<T> a;
             if constexpr (kBf16) {
               a.v = kt[kr * GPR + ((2 * t + hf) ^ swz<GPR>(kr))];
@@ -206,16 +206,30 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
               a.a = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf) ^ swz<GPR>(kr))]);
               a.b = *reinterpret_cast<const float4*>(&kt[kr * GPR + ((4 * t + 2 * hf + 1) ^ swz<GPR>(kr))]);
             }
-            mma_k16(s[is], a, qf[t]);
+            return a;
+          };
+          Frag<T> ka[4];
+          ka[0] = kfrag(0);
+          if constexpr (kQk > 1) ka[1] = kfrag(1);
+          if constexpr (kQk > 2) ka[2] = kfrag(2);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+  #pragma unroll
+          for (int t = 0; t < kQk; ++t) {
+            if (t + 3 < kQk) ka[(t + 3) % 4] = kfrag(t + 3);
+            mma_k16(s[is], ka[t % 4], qf[t]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-        // keys past N exist only in the last, partial key block
+        // keys past N exist only in the last, partial key block.  Element i of subtile is
+        // is key 32is + 8(i/4) + 4hf + i%4: compared as a constant against nv - 4hf, so no
+        // per-element key index stays live across the loop.
         if (nv < KT) {
+          const int nvh = nv - 4 * hf;
   #pragma unroll
           for (int is = 0; is < kSub; ++is)
   #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (32 * is + 8 * (i >> 2) + 4 * hf + (i & 3) >= nv) s[is][i] = -INFINITY;
+              if (32 * is + 8 * (i >> 2) + (i & 3) >= nvh) s[is][i] = -INFINITY;
         }
         // row max of the raw scores (scale > 0 commutes with max), both lane halves
         float mc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // independent chains
@@ -261,43 +275,53 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
             pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
           }
         }
-        // O^T += V^T P^T
+        // O^T += V^T P^T; the V^T fragment of pair p+2 is read before the product of pair
+        // p, in an order fixed with scheduling fences (left to itself the scheduler puts
+        // each read right before its product and waits for it there)
+        auto vfrag = [&](int io, int u) {
+          Frag<T> a;
+          if constexpr (kBf16) {
+            // transpose reads: lane s of 16-lane group g supplies row kbase + s/4, columns
+            // dbase + 4*(s%4) .. +3; lane i of the group receives column dbase + i of rows
+            // kbase .. kbase+3, i.e. V^T[d][4 consecutive keys].
+            const int g = lane >> 4, sl = lane & 15;
+            const int dcol = 32 * io + 16 * (g & 1) + 4 * (sl & 3);
+            short4_t part[2];
   #pragma unroll
-        for (int io = 0; io < kOut; ++io) {
-  #pragma unroll
-          for (int u = 0; u < kPv; ++u) {
-            Frag<T> a;
-            if constexpr (kBf16) {
-              // transpose reads: lane s of 16-lane group g supplies row kbase + s/4, columns
-              // dbase + 4*(s%4) .. +3; lane i of the group receives column dbase + i of rows
-              // kbase .. kbase+3, i.e. V^T[d][4 consecutive keys].
-              const int g = lane >> 4, sl = lane & 15;
-              const int dcol = 32 * io + 16 * (g & 1) + 4 * (sl & 3);
-              short4_t part[2];
-  #pragma unroll
-              for (int tt = 0; tt < 2; ++tt) {
-                const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
-                const int gran = (dcol >> 3) ^ swz<GPR>(kr);
-                const uint16_t* p = vt + kr * D + gran * 8 + (dcol & 7);
-                part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) short4_t*)(p));
-              }
-              const uint2 lo = __builtin_bit_cast(uint2, part[0]);
-              const uint2 hi = __builtin_bit_cast(uint2, part[1]);
-              a.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            } else {
-              const int d = 32 * io + qn;
-              float av[8];
-  #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) {
-                const int kr = 16 * u + 8 * (jj >> 2) + 4 * hf + (jj & 3);
-                av[jj] = vt[(kr * GPR + ((d / G) ^ swz<GPR>(kr))) * G + (d % G)];
-              }
-              a.a = make_float4(av[0], av[1], av[2], av[3]);
-              a.b = make_float4(av[4], av[5], av[6], av[7]);
+            for (int tt = 0; tt < 2; ++tt) {
+              const int kr = 16 * u + 8 * tt + 4 * (g >> 1) + (sl >> 2);
+              const int gran = (dcol >> 3) ^ swz<GPR>(kr);
+              const uint16_t* p = vt + kr * D + gran * 8 + (dcol & 7);
+              part[tt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) short4_t*)(p));
             }
-            mma_k16(acc[io], a, pf[u]);
+            const uint2 lo = __builtin_bit_cast(uint2, part[0]);
+            const uint2 hi = __builtin_bit_cast(uint2, part[1]);
+            a.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          } else {
+            const int d = 32 * io + qn;
+            float av[8];
+  #pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              const int kr = 16 * u + 8 * (jj >> 2) + 4 * hf + (jj & 3);
+              av[jj] = vt[(kr * GPR + ((d / G) ^ swz<GPR>(kr))) * G + (d % G)];
+            }
+            a.a = make_float4(av[0], av[1], av[2], av[3]);
+            a.b = make_float4(av[4], av[5], av[6], av[7]);
           }
+          return a;
+        };
+        constexpr int kPairs = kOut * kPv;
+        Frag<T> va[3];
+        va[0] = vfrag(0, 0);
+        va[1] = vfrag(1 / kPv, 1 % kPv);
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int pp = 0; pp < kPairs; ++pp) {
+          if (pp + 2 < kPairs) va[(pp + 2) % 3] = vfrag((pp + 2) / kPv, (pp + 2) % kPv);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_k16(acc[pp / kPv], va[pp % 3], pf[pp % kPv]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       if (!more) return false;
       e = e_n;
