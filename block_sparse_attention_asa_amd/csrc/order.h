@@ -36,6 +36,8 @@ struct OrderScratch {
   int slice_lo[kOrderClasses];    // this range's slice of each class, in class ranks
   int slice_hi[kOrderClasses];
   int out[kOrderClasses];         // position of the slice's first item
+  int4 slice[kOrderClasses];      // (slice_lo, slice_hi, out - slice_lo) of each class
+  int rank0[kOrderClasses][kOrderThreads];   // each thread's first class rank, per class
 };
 
 template <typename Len>
@@ -43,13 +45,35 @@ __device__ void order_balanced(Len len, int32_t* __restrict__ order, int total, 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int per = (total + kOrderThreads - 1) / kOrderThreads;
   const int t0 = min((int)threadIdx.x * per, total), t1 = min(t0 + per, total);
+  // per-class counts of this thread's run: packed 10 bits each (classes 0-5 in h[0],
+  // 6-11 in h[1]) for runs shorter than 1024 items, one counter each otherwise
+  static_assert(kOrderClasses <= 12, "two words of six 10-bit counters");
   int cnt[kOrderClasses];
+  if (per < 1024) {
+    uint64_t h[2] = {0ull, 0ull};
+    // four lengths per round, loaded together (the last round re-reads item t1-1)
+    for (int i0 = t0; i0 < t1; i0 += 4) {
+      int ln[4];
 #pragma unroll
-  for (int k = 0; k < kOrderClasses; ++k) cnt[k] = 0;
-  for (int i = t0; i < t1; ++i) {
-    const int cl = length_class(len(i));
+      for (int j = 0; j < 4; ++j) ln[j] = len(min(i0 + j, t1 - 1));
 #pragma unroll
-    for (int k = 0; k < kOrderClasses; ++k) cnt[k] += cl == k ? 1 : 0;
+      for (int j = 0; j < 4; ++j) {
+        const int cl = length_class(ln[j]);
+        const uint64_t one = i0 + j < t1 ? 1ull << (10 * (cl % 6)) : 0ull;
+        h[0] += cl < 6 ? one : 0ull;
+        h[1] += cl < 6 ? 0ull : one;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kOrderClasses; ++k) cnt[k] = (int)((h[k / 6] >> (10 * (k % 6))) & 1023ull);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kOrderClasses; ++k) cnt[k] = 0;
+    for (int i = t0; i < t1; ++i) {
+      const int cl = length_class(len(i));
+#pragma unroll
+      for (int k = 0; k < kOrderClasses; ++k) cnt[k] += cl == k ? 1 : 0;
+    }
   }
   // inclusive scan of each class count over the threads of a wavefront, then over waves
   int incl[kOrderClasses];
@@ -75,35 +99,75 @@ __device__ void order_balanced(Len len, int32_t* __restrict__ order, int total, 
     sh.total[k] = run;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {   // this range's slice of every class, longest class first
-    int lo, hi;
-    xcd_range(x, total, lo, hi);
-    int cursor = 0, out = lo;
-    for (int k = kOrderClasses - 1; k >= 0; --k) {
-      const int s = sh.total[k], b = s / kXcds, e = s % kXcds;
-      int start = x * b;
-      for (int j = 0; j < x; ++j) start += ((j - cursor + kXcds) % kXcds) < e ? 1 : 0;
-      const int size = b + (((x - cursor + kXcds) % kXcds) < e ? 1 : 0);
-      sh.slice_lo[k] = start;
-      sh.slice_hi[k] = start + size;
-      sh.out[k] = out;
-      out += size;
-      cursor = (cursor + e) % kXcds;
-    }
+  static_assert((kXcds & (kXcds - 1)) == 0, "XCD count is a power of two");
+  if (threadIdx.x < kOrderClasses) {   // this range's slice of class k (one thread per class)
+    const int k = threadIdx.x;
+    int cursor = 0;   // the XCD that takes class k's first larger slice
+    for (int k2 = kOrderClasses - 1; k2 > k; --k2) cursor += sh.total[k2] & (kXcds - 1);
+    cursor &= kXcds - 1;
+    const int s = sh.total[k], b = s / kXcds, e = s & (kXcds - 1);
+    int start = x * b;
+    for (int j = 0; j < x; ++j) start += ((j - cursor) & (kXcds - 1)) < e ? 1 : 0;
+    sh.slice_lo[k] = start;
+    sh.slice_hi[k] = start + b + (((x - cursor) & (kXcds - 1)) < e ? 1 : 0);
   }
   __syncthreads();
-  int rank[kOrderClasses];   // class rank of this thread's next item of each class
+  if (threadIdx.x < kOrderClasses) {   // slices come longest class first inside the range
+    const int k = threadIdx.x;
+    int lo, hi;
+    xcd_range(x, total, lo, hi);
+    int out = lo;
+    for (int k2 = kOrderClasses - 1; k2 > k; --k2) out += sh.slice_hi[k2] - sh.slice_lo[k2];
+    sh.out[k] = out;
+    sh.slice[k] = make_int4(sh.slice_lo[k], sh.slice_hi[k], out - sh.slice_lo[k], 0);
+  }
+  __syncthreads();
+  // per class: the rank of this thread's next item, and the offset from a rank in this
+  // range's slice to its position (rank + off), selected without branches
+  int rank[kOrderClasses], slo[kOrderClasses], shi[kOrderClasses], off[kOrderClasses];
 #pragma unroll
-  for (int k = 0; k < kOrderClasses; ++k) rank[k] = sh.wsum[wv][k] + incl[k] - cnt[k];
-  for (int i = t0; i < t1; ++i) {
+  for (int k = 0; k < kOrderClasses; ++k) {
+    rank[k] = sh.wsum[wv][k] + incl[k] - cnt[k];
+    slo[k] = sh.slice_lo[k];
+    shi[k] = sh.slice_hi[k];
+    off[k] = sh.out[k] - slo[k];
+  }
+  // a run that holds no rank of this range's slices writes nothing: skip it
+  bool hit = false;
+#pragma unroll
+  for (int k = 0; k < kOrderClasses; ++k) hit |= cnt[k] > 0 && rank[k] < shi[k] && rank[k] + cnt[k] > slo[k];
+  if (per < 1024) {
+    // an item's rank is its thread's first rank of the class (from LDS, this thread's own
+    // column) plus the items of the class before it in the run (packed counters, as above)
+#pragma unroll
+    for (int k = 0; k < kOrderClasses; ++k) sh.rank0[k][threadIdx.x] = rank[k];
+    uint64_t pk[2] = {0ull, 0ull};
+    for (int i = t0; hit && i < t1; ++i) {
+      const int cl = length_class(len(i));
+      const int sub = 10 * (cl % 6);
+      const bool hi6 = cl >= 6;
+      const uint64_t word = hi6 ? pk[1] : pk[0];
+      const int q = sh.rank0[cl][threadIdx.x] + (int)((word >> sub) & 1023ull);
+      pk[0] += hi6 ? 0ull : 1ull << sub;
+      pk[1] += hi6 ? 1ull << sub : 0ull;
+      const int4 si = sh.slice[cl];
+      if (q >= si.x && q < si.y) order[si.z + q] = i;
+    }
+    return;
+  }
+  for (int i = t0; hit && i < t1; ++i) {
     const int cl = length_class(len(i));
+    int q = 0, lo_k = 0, hi_k = 0, off_k = 0;
 #pragma unroll
     for (int k = 0; k < kOrderClasses; ++k) {
-      if (cl == k) {
-        const int q = rank[k]++;
-        if (q >= sh.slice_lo[k] && q < sh.slice_hi[k]) order[sh.out[k] + q - sh.slice_lo[k]] = i;
-      }
+      const bool m = cl == k;
+      q = m ? rank[k] : q;
+      lo_k = m ? slo[k] : lo_k;
+      hi_k = m ? shi[k] : hi_k;
+      off_k = m ? off[k] : off_k;
+      rank[k] += m ? 1 : 0;
     }
+    if (q >= lo_k && q < hi_k) order[off_k + q] = i;
   }
 }
 
