@@ -524,16 +524,26 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
       const uint4* gt = Gs[slot];
       const float* lt = reinterpret_cast<const float*>(Ls[slot]);
 
-      // S = Q K^T, dP = dO V^T (queries on rows, this lane's key on the column)
+      // S = Q K^T, dP = dO V^T (queries on rows, this lane's key on the column); the
+      // operands of k-step t+1 are read before the products of k-step t (scheduling fences)
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      {
+        auto ops = [&](int t, Frag<T>& qa, Frag<T>& ga, Frag<T>& va) {
+          qa.v = qt[qn * GPR + ((2 * t + hf) ^ swz<GPR>(qn))];
+          ga.v = gt[qn * GPR + ((2 * t + hf) ^ swz<GPR>(qn))];
+          va.v = Vf[t][tid];
+        };
+        Frag<T> qa[2], ga[2], va[2];
+        ops(0, qa[0], ga[0], va[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < kQk; ++t) {
-        Frag<T> qa, ga, va;
-        qa.v = qt[qn * GPR + ((2 * t + hf) ^ swz<GPR>(qn))];
-        ga.v = gt[qn * GPR + ((2 * t + hf) ^ swz<GPR>(qn))];
-        va.v = Vf[t][tid];
-        mma_k16(s, qa, kf[t]);
-        mma_k16(dp, ga, va);
+        for (int t = 0; t < kQk; ++t) {
+          if (t + 1 < kQk) ops(t + 1, qa[(t + 1) % 2], ga[(t + 1) % 2], va[(t + 1) % 2]);
+          __builtin_amdgcn_sched_barrier(0);
+          mma_k16(s, qa[t % 2], kf[t]);
+          mma_k16(dp, ga[t % 2], va[t % 2]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // P = exp2(S scale log2e - lse log2e), dS = P (dP - D); queries past nq get 0
       Frag<T> pf[kPv], dsf[kPv];
