@@ -251,33 +251,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
   #pragma unroll
           for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
         }
-        const float neg_m = -m_run;
-        Frag<T> pf[kPv];
-  #pragma unroll
-        for (int u = 0; u < kPv; ++u) {
-          float pv[8];
-  #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_m));
-          if constexpr (kBf16) {
-            uint32_t wd[4];
-  #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bf16x2_t pk = {static_cast<__bf16>(pv[2 * j]), static_cast<__bf16>(pv[2 * j + 1])};
-              wd[j] = __builtin_bit_cast(uint32_t, pk);
-              l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
-            }
-            pf[u].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-          } else {
-  #pragma unroll
-            for (int j = 0; j < 8; ++j) l_run += pv[j];
-            pf[u].a = make_float4(pv[0], pv[1], pv[2], pv[3]);
-            pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
-          }
-        }
-        // O^T += V^T P^T; the V^T fragment of pair p+2 is read before the product of pair
-        // p, in an order fixed with scheduling fences (left to itself the scheduler puts
-        // each read right before its product and waits for it there)
+        // V^T fragment (io, u): rows of key group u (16 keys), columns 32io .. 32io+31
         auto vfrag = [&](int io, int u) {
           Frag<T> a;
           if constexpr (kBf16) {
@@ -311,17 +285,81 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
           }
           return a;
         };
+        const float neg_m = -m_run;
+        Frag<T> pf[kPv];
+        // P^T in bf16, two weights per word, and the row sum of the rounded weights
+        auto p_word = [&](int u, int j) {
+          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * j], scale_log2, neg_m));
+          const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * j + 1], scale_log2, neg_m));
+          const bf16x2_t pk = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+          return __builtin_bit_cast(uint32_t, pk);
+        };
         constexpr int kPairs = kOut * kPv;
-        Frag<T> va[3];
-        va[0] = vfrag(0, 0);
-        va[1] = vfrag(1 / kPv, 1 % kPv);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kBf16 && D == 64) {
+          // O^T += V^T P^T with key group u outer: the weights of group u+1 are formed beside
+          // the products of group u (kOut products, 4/kOut words after each).  At d = 64 the
+          // step is bound by the vector work and this overlap inside the wavefront pays
+          // (CogVideoX-shaped layer -1.9 %); at d = 128 the three wavefronts of a SIMD
+          // already overlap it, and the plain order below is 0.5 % faster.  The V^T
+          // fragment of product p+2 is read before product p; the order is fixed with
+          // scheduling fences.  Every accumulator still adds its groups in order.
+          constexpr int kWords = 4 / kOut;
+          static_assert(kWords * kOut == 4, "whole words per product");
+          uint32_t wd[4];
   #pragma unroll
-        for (int pp = 0; pp < kPairs; ++pp) {
-          if (pp + 2 < kPairs) va[(pp + 2) % 3] = vfrag((pp + 2) / kPv, (pp + 2) % kPv);
+          for (int j = 0; j < 4; ++j) wd[j] = p_word(0, j);
+          pf[0].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          Frag<T> va[3];
+          va[0] = vfrag(0, 0);
+          va[1] = vfrag(1 % kOut, 1 / kOut);
           __builtin_amdgcn_sched_barrier(0);
-          mma_k16(acc[pp / kPv], va[pp % 3], pf[pp % kPv]);
+  #pragma unroll
+          for (int pp = 0; pp < kPairs; ++pp) {
+            const int io = pp % kOut, u = pp / kOut;
+            if (pp + 2 < kPairs) va[(pp + 2) % 3] = vfrag((pp + 2) % kOut, (pp + 2) / kOut);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_k16(acc[io], va[pp % 3], pf[u]);
+            if (u + 1 < kPv) {
+  #pragma unroll
+              for (int j = 0; j < kWords; ++j) wd[kWords * io + j] = p_word(u + 1, kWords * io + j);
+              if (io == kOut - 1) pf[u + 1].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+  #pragma unroll
+          for (int u = 0; u < kPv; ++u) {
+            if constexpr (kBf16) {
+              uint32_t wd[4];
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) wd[j] = p_word(u, j);
+              pf[u].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            } else {
+              float pv[8];
+  #pragma unroll
+              for (int j = 0; j < 8; ++j)
+                pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + j], scale_log2, neg_m));
+  #pragma unroll
+              for (int j = 0; j < 8; ++j) l_run += pv[j];
+              pf[u].a = make_float4(pv[0], pv[1], pv[2], pv[3]);
+              pf[u].b = make_float4(pv[4], pv[5], pv[6], pv[7]);
+            }
+          }
+          // O^T += V^T P^T; the V^T fragment of pair p+2 is read before the product of pair
+          // p, in an order fixed with scheduling fences (left to itself the scheduler puts
+          // each read right before its product and waits for it there)
+          Frag<T> va[3];
+          va[0] = vfrag(0, 0);
+          va[1] = vfrag(1 / kPv, 1 % kPv);
           __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int pp = 0; pp < kPairs; ++pp) {
+            if (pp + 2 < kPairs) va[(pp + 2) % 3] = vfrag((pp + 2) / kPv, (pp + 2) % kPv);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_k16(acc[pp / kPv], va[pp % 3], pf[pp % kPv]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       if (!more) return false;
       e = e_n;
