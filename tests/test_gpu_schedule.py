@@ -140,3 +140,27 @@ def test_csr_and_output_buffer_checks(asa_lib):
         with pytest.raises(ValueError):
             asa.asa_attention_fwd_split(x["q"], x["k"], x["v"], rp, ci, cfg.blk, out=small)
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_order_rule_with_long_runs(asa_lib):
+    """More than 1023 x 1024 rows: each of the builder's threads owns a run of 1024 rows or
+    more, past the packed per-class counters, so the order takes the one-counter-per-class
+    path.  A static mask (no Q or K needed) with four row-length classes."""
+    asa = asa_lib
+    B, H, blk = 4, 256, 128
+    N = 1024 * blk                                    # Nb = 1024: 4 * 256 * 1024 rows
+    cycle = [(gen.DIAG, 0), (gen.VSTRIPE, 3), (gen.MULTIDIAG, 16 * blk), (gen.SKIP, 0)]
+    pats = [cycle[h % len(cycle)] for h in range(H)]
+    say(f"case long runs: B={B} H={H} Nb={N // blk} rows {B * H * (N // blk)}")
+    rp_t, ci_t, order_t = asa.asa_static_mask(B, H, N, blk, pats, "cuda:0", with_order=True)
+    torch.cuda.synchronize()
+    rp = rp_t.cpu().numpy()
+    order = order_t.cpu().numpy().astype(np.int64)
+    del ci_t
+    torch.cuda.empty_cache()
+    assert rp.size - 1 > 1023 * 1024
+    counts = np.diff(rp.astype(np.int64))
+    assert len(set(int(c).bit_length() for c in np.unique(counts))) >= 3
+    exp = expected_order(rp)
+    assert np.array_equal(order, exp), f"first mismatch at {int(np.argmax(order != exp))}"
