@@ -116,6 +116,16 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
 #pragma unroll
   for (int io = 0; io < kOut; ++io) acc[io] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
+  // bf16 inputs: the row sums of the rounded weights run on the matrix cores.  A 4x4x4
+  // product with an all-ones operand adds the four weights a lane holds into that lane's
+  // own accumulator column (its four elements carry the same sum).  A v_dot2 row sum issues
+  // on the matrix pipeline as well but holds up the partner wavefronts' products.
+  f32x4_t l_mma = f32x4_t{};
+  auto psum = [&](const uint4& v) {
+    const short4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};   // bf16 1.0
+    l_mma = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones, __builtin_bit_cast(short4_t, make_uint2(v.x, v.y)), l_mma, 0, 0, 0);
+    l_mma = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones, __builtin_bit_cast(short4_t, make_uint2(v.z, v.w)), l_mma, 0, 0, 0);
+  };
 
   if (e1 > e0) {
     Frag<T> qf[kQk];
@@ -248,6 +258,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
           m_run = m_new;
           l_run *= alpha;
+          l_mma *= alpha;
   #pragma unroll
           for (int io = 0; io < kOut; ++io) acc[io] *= alpha;
         }
@@ -292,7 +303,6 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
           const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * j], scale_log2, neg_m));
           const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u >> 1][8 * (u & 1) + 2 * j + 1], scale_log2, neg_m));
           const bf16x2_t pk = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
           return __builtin_bit_cast(uint32_t, pk);
         };
         constexpr int kPairs = kOut * kPv;
@@ -310,6 +320,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
   #pragma unroll
           for (int j = 0; j < 4; ++j) wd[j] = p_word(0, j);
           pf[0].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+          psum(pf[0].v);
           Frag<T> va[3];
           va[0] = vfrag(0, 0);
           va[1] = vfrag(1 % kOut, 1 / kOut);
@@ -323,7 +334,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
             if (u + 1 < kPv) {
   #pragma unroll
               for (int j = 0; j < kWords; ++j) wd[kWords * io + j] = p_word(u + 1, kWords * io + j);
-              if (io == kOut - 1) pf[u + 1].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+              if (io == kOut - 1) {
+                pf[u + 1].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                psum(pf[u + 1].v);
+              }
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -335,6 +349,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
   #pragma unroll
               for (int j = 0; j < 4; ++j) wd[j] = p_word(u, j);
               pf[u].v = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+              psum(pf[u].v);
             } else {
               float pv[8];
   #pragma unroll
@@ -377,7 +392,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 3
   // epilogue: O = acc / l   (zero for empty rows and skipped heads)
   float l_tot;
   {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l_lane = kBf16 ? l_mma[0] : l_run;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
     l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
   if (kSplit && n_chunks > 1) {
