@@ -583,13 +583,28 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
       // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transpose reads)
       const uint16_t* qtile = reinterpret_cast<const uint16_t*>(qt);
       const uint16_t* gtile = reinterpret_cast<const uint16_t*>(gt);
+      // product p: (io, u) = (p / 2kPv, p / 2 % kPv), dV for even p and dK for odd p; the
+      // transposed operand of product p+3 is read before product p (scheduling fences).
+      // Three ahead: the LDS round trip of each read stays under three products.
+      {
+        constexpr int kProd = 2 * kOut * kPv, AHEAD = 3;
+        auto trf = [&](int p) { return tr_frag<D>((p & 1) ? qtile : gtile, p / (2 * kPv), (p / 2) % kPv, lane); };
+        Frag<T> ta[AHEAD + 1];
 #pragma unroll
-      for (int io = 0; io < kOut; ++io)
+        for (int p = 0; p < AHEAD; ++p) ta[p] = trf(p);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < kPv; ++u) {
-          mma_k16(dv[io], tr_frag<D>(gtile, io, u, lane), pf[u]);
-          mma_k16(dk[io], tr_frag<D>(qtile, io, u, lane), dsf[u]);
+        for (int p = 0; p < kProd; ++p) {
+          if (p + AHEAD < kProd) ta[(p + AHEAD) % (AHEAD + 1)] = trf(p + AHEAD);
+          __builtin_amdgcn_sched_barrier(0);
+          const int io = p / (2 * kPv), u = (p / 2) % kPv;
+          if (p & 1)
+            mma_k16(dk[io], ta[p % (AHEAD + 1)], dsf[u]);
+          else
+            mma_k16(dv[io], ta[p % (AHEAD + 1)], pf[u]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
 
       if (!more) break;
       f = f_n;
