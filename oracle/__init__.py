@@ -5,4 +5,5 @@ from .asa_oracle import (pool, block_scores, block_softmax, rank_order, adaptive
                          to_csr, density, attention, attention_rows, attention_block, dense_attention,
                          kept_tokens, kept_tile_flops, num_blocks, block_range, text_blocks,
                          attention_lse, attention_bwd, attention_bwd_block, attention_bwd_flops,
+                         attention_bwd_terms,
                          pattern_sparsity, pattern_mse, pattern_loss, select_patterns, pattern_search)

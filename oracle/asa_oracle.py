@@ -404,17 +404,24 @@ def attention_lse(Q: np.ndarray, K: np.ndarray, M: np.ndarray, blk: int) -> np.n
     return L
 
 
-def _row_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray):
-    """(dq, dk, dv) of sum(g * softmax(q k^T / sqrt(d)) v) for one set of query rows."""
+def _row_softmax_and_ds(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray):
+    """For one set of query rows: P = softmax(q k^T / sqrt(d)) and dS = P (dP - D), where
+    dP = g v^T and D = rowsum(P dP) (the chain rule through each row softmax)."""
     d = q.shape[-1]
     s = (q @ k.T) / np.sqrt(d)
     s = s - s.max(axis=1, keepdims=True)
     e = np.exp(s)
     P = e / e.sum(axis=1, keepdims=True)
-    dv = P.T @ g
     dP = g @ v.T
     D = (P * dP).sum(axis=1, keepdims=True)
-    ds = P * (dP - D)
+    return P, P * (dP - D)
+
+
+def _row_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray):
+    """(dq, dk, dv) of sum(g * softmax(q k^T / sqrt(d)) v) for one set of query rows."""
+    d = q.shape[-1]
+    P, ds = _row_softmax_and_ds(q, k, v, g)
+    dv = P.T @ g
     dq = (ds @ k) / np.sqrt(d)
     dk = (ds.T @ q) / np.sqrt(d)
     return dq, dk, dv
@@ -442,6 +449,38 @@ def attention_bwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, M
                 dK[b, h, J] += dk
                 dV[b, h, J] += dv
     return dQ, dK, dV
+
+
+def attention_bwd_terms(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, M: np.ndarray,
+                        blk: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Per element of (dQ, dK, dV): the sum of the absolute values of the products that add
+    up to it, float64.  dQ_i sums dS_ij K_j / sqrt(d) over kept keys j, dK_j sums
+    dS_ij Q_i / sqrt(d) and dV_j sums P_ij dO_i over the queries i that keep j.
+
+    A backward that rounds every weight P and every dS to relative precision u before its
+    products is off by at most u times these sums, plus its own accumulation rounding.  For
+    dQ they can exceed |dQ| by far: each row of dS sums to exactly zero, so keys that share a
+    large component cancel in dQ but not in its rounding error."""
+    B, H, N, d = Q.shape
+    Nb = num_blocks(N, blk)
+    tQ = np.zeros((B, H, N, d), dtype=np.float64)
+    tK = np.zeros((B, H, N, d), dtype=np.float64)
+    tV = np.zeros((B, H, N, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for r in range(Nb):
+                J = kept_tokens(M[b, h, r], N, blk)
+                if J.size == 0:
+                    continue
+                lo, hi = block_range(r, N, blk)
+                q = Q[b, h, lo:hi].astype(np.float64)
+                k = K[b, h, J].astype(np.float64)
+                g = dO[b, h, lo:hi].astype(np.float64)
+                P, ds = _row_softmax_and_ds(q, k, V[b, h, J].astype(np.float64), g)
+                tQ[b, h, lo:hi] = (np.abs(ds) @ np.abs(k)) / np.sqrt(d)
+                tK[b, h, J] += (np.abs(ds).T @ np.abs(q)) / np.sqrt(d)
+                tV[b, h, J] += P.T @ np.abs(g)
+    return tQ, tK, tV
 
 
 def attention_bwd_block(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, M: np.ndarray,

@@ -386,6 +386,58 @@ def check_bwd_identical_keys_closed_form():
     assert np.all(dq[0, 0, 32:] == 0) and np.all(dk[0, 0, :32] == 0) and np.all(dv[0, 0, 64:] == 0)
 
 
+def _bf16(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (nearest even, through float32) and back to float64."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def check_bwd_terms_bound_rounded_products():
+    """attention_bwd_terms bounds the gradients of a computation that rounds P and dS to
+    bf16 before the products, and the bound is tight enough to matter.
+
+    Per query block, P and dS = dL/dS come from torch (softmax and autograd of
+    sum(G * softmax(S) V), no formula retyped), are rounded to bf16, and give the gradients
+    through plain matmuls.  Each element's error against attention_bwd must stay within
+    2^-8 times its term sum (the rounding is at most 2^-9 relative).  Keys share a large
+    component in one head, so there dQ cancels and its rounded error exceeds 2^-8 |dQ|
+    by far while staying inside the term bound."""
+    B, H, N, d, blk = 1, 2, 150, 16, 32
+    q, k, v = _qkv(B, H, N, d, 42)
+    k[0, 1] += 40.0                           # head 1: a large component shared by every key
+    g = RNG(43).standard_normal((B, H, N, d))
+    Nb = O.num_blocks(N, blk)
+    M = RNG(44).random((B, H, Nb, Nb)) < 0.6
+    M[0, 0, 2] = False                        # a query block with no kept key block
+    M[0, 1, :, 0] = True
+    dq, dk, dv = O.attention_bwd(q, k, v, g, M, blk)
+    tq, tk, tv = O.attention_bwd_terms(q, k, v, g, M, blk)
+    rq, rk, rv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+    for h in range(H):
+        for r in range(Nb):
+            J = O.kept_tokens(M[0, h, r], N, blk)
+            if J.size == 0:
+                continue
+            lo, hi = O.block_range(r, N, blk)
+            qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q[0, h, lo:hi], k[0, h, J], v[0, h, J]))
+            S = (qt @ kt.T / math.sqrt(d)).requires_grad_(True)
+            P = torch.softmax(S, dim=1)
+            (P @ vt * torch.from_numpy(g[0, h, lo:hi])).sum().backward()
+            Pr, dSr = _bf16(P.detach().numpy()), _bf16(S.grad.numpy())
+            rq[0, h, lo:hi] = dSr @ k[0, h, J] / math.sqrt(d)
+            rk[0, h, J] += dSr.T @ q[0, h, lo:hi] / math.sqrt(d)
+            rv[0, h, J] += Pr.T @ g[0, h, lo:hi]
+    u = 2.0 ** -8
+    for name, r_, x, t in (("dq", rq, dq, tq), ("dk", rk, dk, tk), ("dv", rv, dv, tv)):
+        err = np.abs(r_ - x)
+        assert np.all(err <= u * t + 1e-12), (name, float((err - u * t).max()))
+        assert np.all(np.abs(x) <= t * (1 + 1e-12) + 1e-12), name      # triangle inequality
+        ratio = err[t > 0] / (u * t[t > 0])
+        assert ratio.max() > 0.15, (name, ratio.max())                 # not a loose bound
+    assert np.all(tq[0, 0, 64:96] == 0) and np.all(dq[0, 0, 64:96] == 0)
+    err1, mag1 = np.abs(rq[0, 1] - dq[0, 1]), np.abs(dq[0, 1])
+    assert err1.max() > 4 * u * mag1.max(), (err1.max(), mag1.max())  # cancellation in dQ
+
+
 def check_bwd_blocks_assemble_full():
     """Per-row pieces (attention_bwd_block) add up to the whole-tensor gradients."""
     B, H, N, d, blk = 1, 2, 100, 8, 32
@@ -715,6 +767,7 @@ ALL_CHECKS = [
     check_kept_tile_flops,
     check_bwd_finite_differences, check_bwd_matches_torch_autograd,
     check_bwd_identical_keys_closed_form, check_bwd_blocks_assemble_full, check_lse_matches_scipy,
+    check_bwd_terms_bound_rounded_products,
     check_pattern_sparsity_token_pairs, check_pattern_mse_matches_torch,
     check_pattern_uniform_attention_closed_form, check_select_rule_cases,
     check_search_follows_table3_trends,

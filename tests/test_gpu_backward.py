@@ -265,3 +265,42 @@ def test_backward_full_size_720p_sampled(asa_lib):
     _compare_grad(torch.from_numpy(np.concatenate(got_q)), np.concatenate(ref_q), "dQ sampled")
     _compare_grad(torch.from_numpy(np.concatenate(got_k)), np.concatenate(ref_k), "dK sampled")
     _compare_grad(torch.from_numpy(np.concatenate(got_v)), np.concatenate(ref_v), "dV sampled")
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 3, 2000, 128), (2, 3, 4000, 64)])
+def test_backward_wide_score_range(asa_lib, B, H, N, d):
+    """Scores that climb, fall or stay flat by 90 log2 units across each row's kept blocks
+    (the inputs of the softmax-range forward test), through a key component of up to ~180
+    shared by neighbouring keys.  P = exp2(S - lse) spans weights near 1 down to underflow.
+
+    The backward gets the oracle's O and lse (rounded to fp32), so only its own rounding is
+    measured.  It rounds P and dS to bf16 before the products, so each gradient element may
+    be off by 2^-8 times the sum of the absolute values of its products
+    (attention_bwd_terms), plus fp32 accumulation.  Each row of dS sums to zero, so with
+    large shared key components dQ cancels far below that sum: the relative bound of the
+    other backward tests does not apply to dQ here, the elementwise one does."""
+    from test_gpu_softmax_range import _inputs as wide_inputs, _mask as spread_mask
+    asa = asa_lib
+    blk = 128
+    x, x64 = wide_inputs(B, H, N, d, seed=81)
+    Nb = (N + blk - 1) // blk
+    M = spread_mask(B, H, Nb)
+    say(f"case wide scores: B={B} H={H} N={N} d={d} rows={B * H * Nb}")
+    xd = to_device(x)
+    rp, ci = csr_to_device(M)
+    o = torch.from_numpy(O.attention(x64["q"], x64["k"], x64["v"], M, blk).astype(np.float32)).to("cuda:0")
+    lse = torch.from_numpy(O.attention_lse(x64["q"], x64["k"], M, blk).astype(np.float32)).to("cuda:0")
+    dout = _dout((B, H, N, d), 81)
+    dq, dk, dv = asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], o, dout.to("cuda:0"), lse, rp, ci, blk)
+    torch.cuda.synchronize()
+    g64 = dout.to(torch.float64).numpy()
+    refs = O.attention_bwd(x64["q"], x64["k"], x64["v"], g64, M, blk)
+    terms = O.attention_bwd_terms(x64["q"], x64["k"], x64["v"], g64, M, blk)
+    for got, ref, t, label in zip((dq, dk, dv), refs, terms, ("dQ", "dK", "dV")):
+        g = got.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(g)), label
+        err = np.abs(g - ref)
+        bound = 2.0 ** -8 * t + 1e-5 * float(np.abs(ref).max())
+        say(f"  [{label}, wide scores] max abs err {err.max():.3e} (ref max {np.abs(ref).max():.3e}); "
+            f"max err / bound {float((err / bound).max()):.3f}")
+        assert np.all(err <= bound), f"{label}: {int((err > bound).sum())} elements over the rounding bound"

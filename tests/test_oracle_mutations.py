@@ -224,6 +224,29 @@ def _attention_block_variant(which):
     return f
 
 
+def _bwd_terms_variant(which):
+    def f(Q, K, V, dO, M, blk):
+        B, H, N, d = Q.shape
+        Nb = core.num_blocks(N, blk)
+        tQ, tK, tV = (np.zeros((B, H, N, d)) for _ in range(3))
+        sc = 1.0 if which == "missing_scale" else np.sqrt(d)
+        for b in range(B):
+            for h in range(H):
+                for r in range(Nb):
+                    J = core.kept_tokens(M[b, h, r], N, blk)
+                    if J.size == 0:
+                        continue
+                    lo, hi = core.block_range(r, N, blk)
+                    q, k, v, g = Q[b, h, lo:hi], K[b, h, J], V[b, h, J], dO[b, h, lo:hi]
+                    P, ds = core._row_softmax_and_ds(q, k, v, g)
+                    a = ds if which == "signed_ds" else np.abs(ds)
+                    tQ[b, h, lo:hi] = (a @ np.abs(v if which == "dq_uses_v" else k)) / sc
+                    tK[b, h, J] += (a.T @ np.abs(q)) / sc
+                    tV[b, h, J] += P.T @ np.abs(g)
+        return tQ, tK, tV
+    return f
+
+
 MUTATIONS = {
     "pool_sum_not_mean": ("pool", _pool_sum),
     "pool_zero_padded_partial_block": ("pool", _pool_zero_padded),
@@ -256,6 +279,9 @@ MUTATIONS = {
     "near_tie_every_row_flagged": ("ambiguous_rows", _ambiguous_variant("all")),
     "attention_block_next_block_queries": ("attention_block", _attention_block_variant("next_block_queries")),
     "attention_block_missing_scale": ("attention_block", _attention_block_variant("no_scale")),
+    "bwd_terms_signed_ds": ("attention_bwd_terms", _bwd_terms_variant("signed_ds")),
+    "bwd_terms_dq_uses_v": ("attention_bwd_terms", _bwd_terms_variant("dq_uses_v")),
+    "bwd_terms_missing_scale": ("attention_bwd_terms", _bwd_terms_variant("missing_scale")),
 }
 
 
