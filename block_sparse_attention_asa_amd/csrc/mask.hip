@@ -113,7 +113,11 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
   constexpr int VEC = 8;
   constexpr int TPR = D / VEC;          // threads per token row
   constexpr int RPP = kThreads / TPR;   // token rows per pass
-  __shared__ double red[RPP][D];        // per-thread partial sums, one row per row group
+  // per-thread partial sums, one row per row group; each thread's VEC columns are followed
+  // by one unused double, so that the lanes of a store (VEC apart) and the lanes of the
+  // column sums (consecutive columns) fall on different banks
+  constexpr int kRedRow = TPR * (VEC + 1);
+  __shared__ double red[RPP][kRedRow];
 
   const int row = blockIdx.x;
   const int bh = row / Nb, r = row - bh * Nb;
@@ -157,13 +161,15 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
       acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
     }
   }
+  const int cg = t % TPR;   // col = cg * VEC
 #pragma unroll
-  for (int j = 0; j < VEC; ++j) red[sub][col + j] = acc[j];
+  for (int j = 0; j < VEC; ++j) red[sub][cg * (VEC + 1) + j] = acc[j];
   __syncthreads();
   if (t < D) {   // one thread per column sums the row groups in a fixed order
+    const int slot = t + t / VEC;
     double v = 0.0;
 #pragma unroll
-    for (int s = 0; s < RPP; ++s) v += red[s][t];
+    for (int s = 0; s < RPP; ++s) v += red[s][slot];
     const double nn = (double)n;
     if (blockIdx.y == 0) qp[(size_t)row * D + t] = v / nn;
     else kpt[((size_t)bh * D + t) * Nb + r] = v / nn;
