@@ -606,18 +606,16 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(const uint32_t* __rest
   for (int k = 0; k < kRowsPerFillWave; ++k) {
     const int rr = wv * kRowsPerFillWave + k, row = row0 + rr;
     if (row >= rows) break;
-    uint32_t w = lane < words ? bits[(size_t)row * words + lane] : 0u;
-    const int pc = __popc(w);
-    int incl = pc;   // inclusive prefix over lanes
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    int out = start[rr] + incl - pc;
-    while (w) {
-      const int b = __ffs(w) - 1;
-      col_idx[out++] = lane * 32 + b;
-      w &= w - 1u;
+    // 64 key blocks per pass, one per lane: lanes 0-31 test bits of word 2p, lanes 32-63
+    // of word 2p+1; a ballot and the lane's rank among the set lanes place each index
+    const uint32_t w = lane < words ? bits[(size_t)row * words + lane] : 0u;
+    int out = start[rr];
+    for (int p = 0; 2 * p < words; ++p) {
+      const uint32_t wl = __shfl(w, 2 * p + (lane >> 5), 64);
+      const bool set = (wl >> (lane & 31)) & 1u;
+      const uint64_t m = __ballot(set);
+      if (set) col_idx[out + __popcll(m & ((1ull << lane) - 1ull))] = 64 * p + lane;
+      out += __popcll(m);
     }
   }
 }
