@@ -111,20 +111,12 @@ __global__ __launch_bounds__(kCscThreads) void csc_kernel(const int32_t* __restr
   int cnt = 0;
   if (c < Nb)
     for (int w = 0; w < words; ++w) cnt += __popc(bitT[c * words + w]);
-  int incl = cnt;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
+  const int incl = wave_incl_sum(cnt);
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
   if (wv == 0) {
     const int v0 = lane < kCscThreads / 64 ? wsum[lane] : 0;
-    int x = v0;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(x, off, 64);
-      if (lane >= off) x += v;
-    }
+    const int x = wave_incl_sum(v0);
     if (lane < kCscThreads / 64) wsum[lane] = x - v0;
   }
   __syncthreads();

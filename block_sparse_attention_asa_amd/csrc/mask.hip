@@ -586,18 +586,14 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(const uint32_t* __rest
   // offset of row0: counts of rows 0 .. row0-1
   int part = 0;
   for (int i = tid; i < row0; i += kCsrThreads) part += count[i];
-  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-  if (lane == 0) wsum[wv] = part;
+  part = wave_incl_sum(part);
+  if (lane == 63) wsum[wv] = part;
   __syncthreads();
   if (wv == 0) {
     int base = 0;
     for (int w = 0; w < kFillWaves; ++w) base += wsum[w];
     const int cnt = row0 + lane < rows ? count[row0 + lane] : 0;   // kFillRows == 64 lanes
-    int incl = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
+    const int incl = wave_incl_sum(cnt);
     start[lane] = base + incl - cnt;
     if (row0 + lane < rows) row_ptr[row0 + lane + 1] = base + incl;
     if (row0 == 0 && lane == 0) row_ptr[0] = 0;
@@ -607,11 +603,14 @@ __global__ __launch_bounds__(kCsrThreads) void csr_kernel(const uint32_t* __rest
     const int rr = wv * kRowsPerFillWave + k, row = row0 + rr;
     if (row >= rows) break;
     // 64 key blocks per pass, one per lane: lanes 0-31 test bits of word 2p, lanes 32-63
-    // of word 2p+1; a ballot and the lane's rank among the set lanes place each index
+    // of word 2p+1 (read from the lanes that loaded them); a ballot and the lane's rank
+    // among the set lanes place each index
     const uint32_t w = lane < words ? bits[(size_t)row * words + lane] : 0u;
     int out = start[rr];
     for (int p = 0; 2 * p < words; ++p) {
-      const uint32_t wl = __shfl(w, 2 * p + (lane >> 5), 64);
+      const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)w, 2 * p);
+      const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)w, 2 * p + 1);
+      const uint32_t wl = lane < 32 ? w0 : w1;
       const bool set = (wl >> (lane & 31)) & 1u;
       const uint64_t m = __ballot(set);
       if (set) col_idx[out + __popcll(m & ((1ull << lane) - 1ull))] = 64 * p + lane;

@@ -30,6 +30,20 @@ constexpr int kOrderClasses = 12;   // lengths <= kMaxMaskBlocks = 2^10 -> class
 
 __device__ inline int length_class(int c) { return c <= 0 ? 0 : 32 - __clz(c); }
 
+// Inclusive sum over the lanes of a wavefront (lane i gets lanes 0..i) by DPP lane moves:
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then row 0's total broadcast into
+// rows 1 and 3 and rows 0-1's total into rows 2 and 3.  It stays in the vector ALU; a
+// scan by shuffles goes through the LDS crossbar once per step.
+__device__ inline int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2, 3
+  return v;
+}
+
 struct OrderScratch {
   int wsum[kOrderThreads / 64][kOrderClasses];
   int total[kOrderClasses];
@@ -79,47 +93,46 @@ __device__ void order_balanced(Len len, int32_t* __restrict__ order, int total, 
   int incl[kOrderClasses];
 #pragma unroll
   for (int k = 0; k < kOrderClasses; ++k) {
-    int v = cnt[k];
-    for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(v, off, 64);
-      if (lane >= off) v += u;
-    }
+    const int v = wave_incl_sum(cnt[k]);
     incl[k] = v;
     if (lane == 63) sh.wsum[wv][k] = v;
   }
   __syncthreads();
-  if (threadIdx.x < kOrderClasses) {   // exclusive wave offsets and class totals
-    const int k = threadIdx.x;
-    int run = 0;
-    for (int w = 0; w < kOrderThreads / 64; ++w) {
-      const int v = sh.wsum[w][k];
-      sh.wsum[w][k] = run;
-      run += v;
-    }
-    sh.total[k] = run;
-  }
-  __syncthreads();
   static_assert((kXcds & (kXcds - 1)) == 0, "XCD count is a power of two");
-  if (threadIdx.x < kOrderClasses) {   // this range's slice of class k (one thread per class)
-    const int k = threadIdx.x;
-    int cursor = 0;   // the XCD that takes class k's first larger slice
-    for (int k2 = kOrderClasses - 1; k2 > k; --k2) cursor += sh.total[k2] & (kXcds - 1);
-    cursor &= kXcds - 1;
-    const int s = sh.total[k], b = s / kXcds, e = s & (kXcds - 1);
+  static_assert(kOrderClasses <= 64, "one lane per class");
+  if (wv == 0) {
+    // lane k < kOrderClasses: exclusive wave offsets and the total of class k
+    int tot = 0;
+    if (lane < kOrderClasses) {
+      int run = 0;
+      for (int w = 0; w < kOrderThreads / 64; ++w) {
+        const int v = sh.wsum[w][lane];
+        sh.wsum[w][lane] = run;
+        run += v;
+      }
+      tot = run;
+    }
+    // this range's slice of class k: the cursor (the XCD that takes class k's first larger
+    // slice) is the sum of total mod 8 over the longer classes, i.e. over the lanes above
+    const int e = tot & (kXcds - 1), b = tot / kXcds;
+    const int incl_e = wave_incl_sum(e);
+    const int cursor = (__builtin_amdgcn_readlane(incl_e, 63) - incl_e) & (kXcds - 1);
     int start = x * b;
     for (int j = 0; j < x; ++j) start += ((j - cursor) & (kXcds - 1)) < e ? 1 : 0;
-    sh.slice_lo[k] = start;
-    sh.slice_hi[k] = start + b + (((x - cursor) & (kXcds - 1)) < e ? 1 : 0);
-  }
-  __syncthreads();
-  if (threadIdx.x < kOrderClasses) {   // slices come longest class first inside the range
-    const int k = threadIdx.x;
+    const int size = lane < kOrderClasses ? b + (((x - cursor) & (kXcds - 1)) < e ? 1 : 0) : 0;
+    // slices come longest class first inside the range: class k starts after the slices of
+    // the classes above it
+    const int incl_s = wave_incl_sum(size);
     int lo, hi;
     xcd_range(x, total, lo, hi);
-    int out = lo;
-    for (int k2 = kOrderClasses - 1; k2 > k; --k2) out += sh.slice_hi[k2] - sh.slice_lo[k2];
-    sh.out[k] = out;
-    sh.slice[k] = make_int4(sh.slice_lo[k], sh.slice_hi[k], out - sh.slice_lo[k], 0);
+    const int out = lo + __builtin_amdgcn_readlane(incl_s, 63) - incl_s;
+    if (lane < kOrderClasses) {
+      sh.total[lane] = tot;
+      sh.slice_lo[lane] = start;
+      sh.slice_hi[lane] = start + size;
+      sh.out[lane] = out;
+      sh.slice[lane] = make_int4(start, start + size, out - start, 0);
+    }
   }
   __syncthreads();
   // per class: the rank of this thread's next item, and the offset from a rank in this
