@@ -240,7 +240,7 @@ __device__ inline void rank_stage(uint64_t (&kv)[RI][PER], int lane) {
 #pragma unroll
       for (int j = 0; j < RI; ++j) {
         const uint64_t a = kv[j][e];
-        const uint64_t b = (uint64_t)__shfl_xor((long long)a, LJ, 64);
+        const uint64_t b = lane_xor64<LJ>(a);
         const bool keep = (a > b) == hi;
         kv[j][e] = keep ? a : b;
       }
@@ -254,17 +254,35 @@ __device__ inline void rank_sort_desc(uint64_t (&kv)[RI][PER], int lane) {
   if constexpr (KK < NP2) rank_sort_desc<PER, RI, NP2, KK * 2>(kv, lane);
 }
 
-__device__ inline double wave_max(double v) {
-  for (int off = 32; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
-  return v;
+// Butterfly reductions over the wavefront (every lane ends with the same bits), exchanging
+// with lanes 32, 16, .., 1 apart.
+template <int LJ>
+__device__ inline double lane_xor_f64(double v) {
+  return __builtin_bit_cast(double, lane_xor64<LJ>(__builtin_bit_cast(uint64_t, v)));
 }
-__device__ inline double wave_sum(double v) {   // butterfly: every lane gets the same bits
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+__device__ inline double wave_max(double v) {
+  v = fmax(v, lane_xor_f64<32>(v));
+  v = fmax(v, lane_xor_f64<16>(v));
+  v = fmax(v, lane_xor_f64<8>(v));
+  v = fmax(v, lane_xor_f64<4>(v));
+  v = fmax(v, lane_xor_f64<2>(v));
+  return fmax(v, lane_xor_f64<1>(v));
+}
+__device__ inline double wave_sum(double v) {
+  v += lane_xor_f64<32>(v);
+  v += lane_xor_f64<16>(v);
+  v += lane_xor_f64<8>(v);
+  v += lane_xor_f64<4>(v);
+  v += lane_xor_f64<2>(v);
+  return v + lane_xor_f64<1>(v);
 }
 __device__ inline int wave_min_int(int v) {
-  for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  return v;
+  v = min(v, (int)lane_xor<32>((uint32_t)v));
+  v = min(v, (int)lane_xor<16>((uint32_t)v));
+  v = min(v, (int)lane_xor<8>((uint32_t)v));
+  v = min(v, (int)lane_xor<4>((uint32_t)v));
+  v = min(v, (int)lane_xor<2>((uint32_t)v));
+  return min(v, (int)lane_xor<1>((uint32_t)v));
 }
 
 __device__ inline uint64_t readlane64(uint64_t v, int l) {

@@ -34,6 +34,34 @@ __device__ inline int length_class(int c) { return c <= 0 ? 0 : 32 - __clz(c); }
 // shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then row 0's total broadcast into
 // rows 1 and 3 and rows 0-1's total into rows 2 and 3.  It stays in the vector ALU; a
 // scan by shuffles goes through the LDS crossbar once per step.
+// The value held by lane (lane ^ LJ) of the wavefront, without the LDS crossbar: DPP quad
+// permutations (LJ = 1, 2), row shifts up and down with a select on the lane's bit (4, 8),
+// and the gfx950 row-swap instructions (16: rows 0<->1 and 2<->3, 32: halves).
+template <int LJ>
+__device__ inline uint32_t lane_xor(uint32_t v) {
+  static_assert(LJ == 1 || LJ == 2 || LJ == 4 || LJ == 8 || LJ == 16 || LJ == 32, "lane distance");
+  const int x = (int)v;
+  if constexpr (LJ == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (LJ == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (LJ == 4 || LJ == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x100 + LJ, 0xf, 0xf, false);   // row_shl: lane + LJ
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x110 + LJ, 0xf, 0xf, false);   // row_shr: lane - LJ
+    return (uint32_t)((__lane_id() & LJ) ? dn : up);
+  } else if constexpr (LJ == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? p[0] : p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? p[0] : p[1];
+  }
+}
+template <int LJ>
+__device__ inline uint64_t lane_xor64(uint64_t v) {
+  return ((uint64_t)lane_xor<LJ>((uint32_t)(v >> 32)) << 32) | lane_xor<LJ>((uint32_t)v);
+}
+
 __device__ inline int wave_incl_sum(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
   v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
