@@ -449,10 +449,13 @@ __global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __r
         atomicOr(&word[rr][c >> 5], 1u << (c & 31));
       }
     }
-    for (int c = lane; c < Nb; c += 64) {
-      const bool forced = (p.keep_diag && c == r) || (c < p.n_text_blocks) ||
-                          static_keep(pid, prm, r, c, g.N, g.blk, Nb);
-      if (forced) atomicOr(&word[rr][c >> 5], 1u << (c & 31));
+    if (p.keep_diag && lane == (r & 63)) atomicOr(&word[rr][r >> 5], 1u << (r & 31));
+    // text columns and the head's static pattern (none for an adaptive-only head)
+    if (p.n_text_blocks > 0 || pid != 0) {
+      for (int c = lane; c < Nb; c += 64) {
+        const bool forced = (c < p.n_text_blocks) || static_keep(pid, prm, r, c, g.N, g.blk, Nb);
+        if (forced) atomicOr(&word[rr][c >> 5], 1u << (c & 31));
+      }
     }
   };
 
