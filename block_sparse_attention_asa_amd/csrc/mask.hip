@@ -177,7 +177,9 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 }
 
 // ------------------------------------------------------------------ block scores + selection
-// One workgroup owns kRankRows consecutive query-block rows of one head.
+// One workgroup owns `rows` (at most kRankRows) consecutive query-block rows of one head;
+// the launch picks `rows` (rank_rows) so that the selection work spreads evenly over the
+// compute units.
 //
 // Scores: S = Qp KpT / sqrt(d) for those rows against all Nb key blocks, a dense float64
 // contraction on the fp64 matrix cores (v_mfma_f64_16x16x4f64), written to LDS.  Operand
@@ -201,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const void* __restrict__
 // order: a bitonic network sorts the NP2 slots, where exchanges at distance J < PER stay
 // inside a lane's registers and the others cross lanes at distance J / PER; RI rows go
 // through the network side by side for instruction-level parallelism.
-constexpr int kRankRows = 16;
+constexpr int kRankRows = 16;       // rows of the score tile (the fp64 MFMA's 16 rows)
+constexpr int kComputeUnits = 256;  // MI355X
 constexpr int rank_threads(int d) { return d >= 128 ? 1024 : 512; }
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
@@ -339,7 +342,7 @@ __device__ inline uint64_t select_kth(const uint64_t (&kv)[PER], const uint64_t 
   return piv;
 }
 
-// grid = B*H*ceil(Nb/kRankRows) workgroups; NP2 = max(64, Nb rounded up to a power of two).
+// grid = B*H*ceil(Nb/rows) workgroups; NP2 = max(64, Nb rounded up to a power of two).
 // The ids an XCD receives map onto one contiguous range of row tiles, so the tiles of a
 // head (which all read that head's KpT) share an L2.
 template <int D, int NP2>
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __r
                                                         const double* __restrict__ kpt,
                                                         uint32_t* __restrict__ bits,
                                                         int32_t* __restrict__ count, MaskGeom g,
-                                                        AdaptiveParams p, HeadTable heads) {
+                                                        AdaptiveParams p, HeadTable heads, int rows) {
   constexpr int kRankThreads = rank_threads(D);
   constexpr int kRankWaves = kRankThreads / 64;
   constexpr int kRankRowsPerWave = kRankRows / kRankWaves;
@@ -359,15 +362,15 @@ __global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __r
   __shared__ double qtile[kRankRows][D + 1];   // the rows' pooled queries (padded rows)
 
   const int Nb = g.Nb;
-  const int tiles = (Nb + kRankRows - 1) / kRankRows;
+  const int tiles = (Nb + rows - 1) / rows;
   int lo, hi;
   xcd_range((int)(blockIdx.x % kXcds), g.B * g.H * tiles, lo, hi);
   const int tile = lo + (int)(blockIdx.x / kXcds);
-  const int bh = tile / tiles, r0 = (tile - bh * tiles) * kRankRows, h = bh % g.H;
+  const int bh = tile / tiles, r0 = (tile - bh * tiles) * rows, h = bh % g.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int pid = heads.id[h], prm = heads.param[h];
   const size_t row0 = (size_t)bh * Nb + r0;
-  const int nrows = min(kRankRows, Nb - r0);
+  const int nrows = min(rows, Nb - r0);   // the score tile's rows past nrows are not used
 
   if (pid == 2) {   // skip head: empty rows
     for (int i = tid; i < nrows * g.words; i += kRankThreads) bits[row0 * g.words + i] = 0u;
@@ -467,6 +470,7 @@ __global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __r
     const int m = min(max(p.k, 0), Nb);
     for (int t = 0; t < kRankRowsPerWave; ++t) {
       const int rr = w * kRankRowsPerWave + t;
+      if (rr >= nrows) break;   // no barrier in this loop
       uint64_t kv[PER], real[PER];
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
@@ -483,8 +487,11 @@ __global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __r
     // sorted, RI at a time.
     for (int pass = 0; pass < kRankRowsPerWave / RI; ++pass) {
       const int rr0 = w * kRankRowsPerWave + pass * RI;   // first tile row of this pass
-      uint64_t kv[RI][PER];
-      double z[RI];
+      // a pass past the tile's rows skips its work but not the barrier
+      const bool live = rr0 < nrows;
+      uint64_t kv[RI][PER] = {};
+      double z[RI] = {};
+      if (live) {
 #pragma unroll
       for (int j = 0; j < RI; ++j) {
         double* sr = srow[rr0 + j];
@@ -511,9 +518,10 @@ __global__ __launch_bounds__(rank_threads(D)) void rank_kernel(const double* __r
         }
       }
       rank_sort_desc<PER, RI, NP2, 2>(kv, lane);
+      }
       __syncthreads();   // numerators visible to every lane
 #pragma unroll
-      for (int j = 0; j < RI; ++j) {
+      for (int j = 0; j < RI && live; ++j) {
         const int rr = rr0 + j;
         // running mass in rank order: a sequential sum over each lane's slots, then a
         // wavefront scan of the lane totals; the first rank reaching tau ends the prefix
@@ -682,19 +690,33 @@ hipError_t launch_pool(const void* q, const void* k, bool bf16, const MaskGeom& 
   return hipGetLastError();
 }
 
+// Rows per rank workgroup.  A launch of fewer than one 16-row workgroup per compute unit
+// takes the fewest rows (down to 8) that still keep it to one workgroup per unit: the
+// selection, bound by each unit's scalar issue, then has fewer rows per unit and every
+// unit works.  Larger launches keep 16 (fewer workgroups reading KpT).
+static int rank_rows(const MaskGeom& g) {
+  const long heads = (long)g.B * g.H;
+  if (heads * ((g.Nb + kRankRows - 1) / kRankRows) >= kComputeUnits) return kRankRows;
+  int rows = kRankRows;
+  for (int r = kRankRows - 1; r >= 8; --r)
+    if (heads * ((g.Nb + r - 1) / r) <= kComputeUnits) rows = r;
+  return rows;
+}
+
 template <int D>
 static hipError_t launch_rank_d(const MaskGeom& g, const AdaptiveParams& p, const HeadTable& heads,
                                 const MaskWorkspace& ws, hipStream_t s) {
-  const int tiles = (g.Nb + kRankRows - 1) / kRankRows;
+  const int rows = rank_rows(g);
+  const int tiles = (g.Nb + rows - 1) / rows;
   const dim3 grid((unsigned)(g.B * g.H * tiles)), block(rank_threads(D));
   int np2 = 64;
   while (np2 < g.Nb) np2 <<= 1;
   switch (np2) {
-    case 64: hipLaunchKernelGGL((rank_kernel<D, 64>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
-    case 128: hipLaunchKernelGGL((rank_kernel<D, 128>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
-    case 256: hipLaunchKernelGGL((rank_kernel<D, 256>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
-    case 512: hipLaunchKernelGGL((rank_kernel<D, 512>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
-    default: hipLaunchKernelGGL((rank_kernel<D, 1024>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads); break;
+    case 64: hipLaunchKernelGGL((rank_kernel<D, 64>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads, rows); break;
+    case 128: hipLaunchKernelGGL((rank_kernel<D, 128>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads, rows); break;
+    case 256: hipLaunchKernelGGL((rank_kernel<D, 256>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads, rows); break;
+    case 512: hipLaunchKernelGGL((rank_kernel<D, 512>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads, rows); break;
+    default: hipLaunchKernelGGL((rank_kernel<D, 1024>), grid, block, 0, s, ws.qp, ws.kpt, ws.bits, ws.count, g, p, heads, rows); break;
   }
   return hipGetLastError();
 }
