@@ -1,5 +1,6 @@
-// Work schedules for the attention kernels (device code shared by the mask builders and
-// the backward).  Nothing here is exported from the shared library.
+// Work schedules for the attention kernels, and the wavefront exchanges and scans they and
+// the mask kernels use (device code shared by the mask builders and the backward).
+// Nothing here is exported from the shared library.
 #pragma once
 
 #include <hip/hip_runtime.h>
