@@ -315,6 +315,18 @@ def main():
 
     result_extra = {"attn_ms_p10_p50_p90": pct(attn_t), "mask_ms_p10_p50_p90": pct(mask_t),
                     "step_ms_p10_p50_p90": pct(step_t)}
+    # the mask build alone, 20 builds back to back: Q and K are read from wherever the
+    # previous build left them (in the step they come back from HBM after the attention)
+    mev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+    build_mask()
+    torch.cuda.synchronize()
+    mev[0].record(stream)
+    for i in range(20):
+        build_mask()
+        mev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    b2b = np.array([mev[i].elapsed_time(mev[i + 1]) for i in range(20)])
+    result_extra["mask_ms_back_to_back"] = round(float(np.median(b2b)), 4)
     if not args.no_graph:
         # the same step captured once in a HIP graph and replayed (no host launches)
         side = torch.cuda.Stream(dev)
