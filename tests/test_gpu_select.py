@@ -62,3 +62,27 @@ def test_selection_sweep(asa_lib, Nb, blk, d, structure):
         n_amb += a
         n_diff += b
     say(f"  {len(ks)} top-k and 6 mass-prefix settings: ambiguous rows {n_amb}, differing rows {n_diff}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_selection_thirteen_row_tiles(asa_lib, d):
+    """12 heads x 256 blocks is fewer than one 16-row workgroup per compute unit, so the
+    builder takes 13 rows per workgroup: the last pass of a workgroup holds one real row
+    (and at d = 64, where a wavefront sorts two rows side by side, one row of the next
+    tile that it must not write).  Top-k and the mass prefix, bit for bit against the
+    oracle except near-tie rows."""
+    asa = asa_lib
+    cfg = gen.Config(name=f"select_13rows_d{d}", seed=77 + d, B=1, H=12, N=256 * 64 - 13, d=d, blk=64,
+                     dtype="bf16", frames=1, Hs=1, Ws=256 * 64 - 13, structure="smooth", mode=gen.TOPK, k=1)
+    assert cfg.Nb == 256 and cfg.B * cfg.H * ((cfg.Nb + 15) // 16) < 256   # 16-row workgroups
+    say(f"case {cfg.name}: N={cfg.N} blk=64 d={d}")
+    x = gen.make_inputs(cfg)
+    xd = to_device(x)
+    q64, k64, _ = oracle_inputs(x)
+    n_amb = n_diff = 0
+    for mode, k, tau, k_cap, diag in ((gen.TOPK, 26, 0.0, 0, 1), (gen.TOPK, 3, 0.0, 0, 0),
+                                      (gen.TAU, 0, 0.9, 0, 1), (gen.TAU, 0, 0.5, 20, 0)):
+        a, b = _check(asa, xd, q64, k64, 64, mode, k, tau, k_cap, diag)
+        n_amb += a
+        n_diff += b
+    say(f"  ambiguous rows {n_amb}, differing rows {n_diff}")
