@@ -391,8 +391,8 @@ def asa_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torc
     _require_device(q, k, v, o, dout, lse, row_ptr, col_idx)
     if not (q.shape == k.shape == v.shape == o.shape == dout.shape):
         raise ValueError("q, k, v, o and dout must share one shape")
-    if not (q.dtype == k.dtype == v.dtype == dout.dtype == torch.bfloat16):
-        raise ValueError("the backward takes bfloat16 q, k, v and dout")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("the backward takes q, k, v and dout of one dtype, bfloat16 or float32")
     shp = _shape_of(q, blk)
     B, H, N, d = q.shape
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):

@@ -215,7 +215,7 @@ size_t split_workspace_layout(const asa_shape* s, int split_max, float** part_o,
 
 extern "C" {
 
-int32_t asa_version(void) { return 10700; }
+int32_t asa_version(void) { return 10800; }
 
 const char* asa_status_string(asa_status st) {
   switch (st) {
@@ -429,8 +429,6 @@ asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const 
   g_last_error[0] = '\0';
   asa_status st = check_shape(shape, true);
   if (st != ASA_OK) return st;
-  if (shape->in_dtype != ASA_BF16)
-    return fail(ASA_ERR_UNSUPPORTED, "the backward takes ASA_BF16 inputs (in_dtype=%d)", shape->in_dtype);
   if (!Q || !K || !V || !O || !dO || !lse) return fail(ASA_ERR_NULL_ARG, "Q, K, V, O, dO or lse is NULL");
   if (!dQ || !dK || !dV) return fail(ASA_ERR_NULL_ARG, "dQ, dK or dV is NULL");
   if (o_dtype != ASA_F32 && o_dtype != ASA_BF16)
@@ -452,6 +450,7 @@ asa_status asa_attention_bwd(const void* Q, const void* K, const void* V, const 
   a.col_idx = csr->col_idx;
   a.order = csr->order;
   a.o_bf16 = o_dtype == ASA_BF16;
+  a.in_f32 = shape->in_dtype == ASA_F32;
   const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)shape->d);
   a.scale = (float)sc;
   a.scale_log2 = (float)(sc * 1.4426950408889634);

@@ -115,6 +115,7 @@ struct BwdArgs {
   float* ld;               // [B*H*N][2] (lse * log2(e), D = dO . O) per query (workspace)
   int32_t B, H, N, d, blk, Nb;
   bool o_bf16;
+  bool in_f32;             // Q, K, V, dO are fp32 (else bf16)
   float scale;             // softmax scale
   float scale_log2;        // scale * log2(e)
   uint32_t skip_bits[kMaxHeads / 32];

@@ -1,4 +1,4 @@
-// Block-sparse attention backward for gfx950 (MI355X), bf16 inputs, fp32 gradients.
+// Block-sparse attention backward for gfx950 (MI355X), bf16 or fp32 inputs, fp32 gradients.
 //
 // The gradients of the masked attention of Sparse-vDiT ("Sparse-vDiT: Sparse Attention
 // Acceleration for Video Diffusion Transformers", section 三 "核心公式"); BLADE
@@ -27,6 +27,8 @@
 //                    of every query block that
 //                    keeps it stream through an LDS ring; per 32-query step
 //                    S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P, dK^T += Q^T dS.
+//   dq_f32_kernel, dkv_f32_kernel   the same two passes for fp32 inputs (P and dS in
+//                    fp32, operands read from global memory; see their section).
 // Each gradient element is accumulated by one lane in a fixed order (no atomics), so the
 // results are deterministic.
 #include <hip/hip_runtime.h>
@@ -41,8 +43,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ preprocessing
 // TPQ = D/8 consecutive threads per query, 8 elements each; D reduced with shuffles.
-template <typename TO, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ dout,
+// Eight consecutive elements of a bf16 (uint16_t) or fp32 row as fp32.
+__device__ inline void load8(const uint16_t* p, float (&x)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(aw[j] << 16);
+    x[2 * j + 1] = __uint_as_float(aw[j] & 0xffff0000u);
+  }
+}
+__device__ inline void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+template <typename TG, typename TO, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const TG* __restrict__ dout,
                                                        const TO* __restrict__ o,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ ld, size_t nq) {
@@ -52,28 +71,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   const int part = (int)(gid % TPQ);
   float acc = 0.f;
   if (q < nq) {
-    const uint4 g = *reinterpret_cast<const uint4*>(dout + q * D + part * 8);
-    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    float gv[8];
+    load8(dout + q * D + part * 8, gv);
     float ov[8];
-    if constexpr (sizeof(TO) == 4) {
-      const float4 a = *reinterpret_cast<const float4*>(o + q * D + part * 8);
-      const float4 b = *reinterpret_cast<const float4*>(o + q * D + part * 8 + 4);
-      ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
-      ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
-    } else {
-      const uint4 a = *reinterpret_cast<const uint4*>(o + q * D + part * 8);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+    load8(o + q * D + part * 8, ov);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ov[2 * j] = __uint_as_float(aw[j] << 16);
-        ov[2 * j + 1] = __uint_as_float(aw[j] & 0xffff0000u);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = __builtin_fmaf(__uint_as_float(gw[j] << 16), ov[2 * j], acc);
-      acc = __builtin_fmaf(__uint_as_float(gw[j] & 0xffff0000u), ov[2 * j + 1], acc);
-    }
+    for (int j = 0; j < 8; ++j) acc = __builtin_fmaf(gv[j], ov[j], acc);
   }
   for (int off = TPQ / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (q < nq && part == 0) {
@@ -612,14 +615,209 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// ------------------------------------------------------------------ fp32 inputs
+// fp32 Q, K, V and dO: the same products on the fp32 matrix cores (eight
+// v_mfma_f32_32x32x2f32 per 16-wide k-step, through mma_k16) with P and dS kept in fp32.
+// One such product does 4096 flops for 512 bytes of operands at an eighth of the bf16
+// product's rate, so operand traffic is no constraint here: every wavefront reads its
+// fragments straight from global memory (the wavefronts of a workgroup share them through
+// the caches), with no LDS staging and no barriers.  Reads of keys or queries past N are
+// clamped to the last valid row of the block, and those elements get weight 0.
+
+// Column fragment: element j = rows[r(j) * D + col], r(j) = r0 + 8(j/4) + 4hf + j%4 clamped
+// to `last` (the k order of the 32x32 output layout, as for the transposed bf16 fragments).
+template <int D>
+__device__ inline Frag<float> col_frag(const float* rows, int r0, int hf, int last, int col) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = min(r0 + 8 * (j >> 2) + 4 * hf + (j & 3), last);
+    v[j] = rows[(size_t)r * D + col];
+  }
+  Frag<float> f;
+  f.a = make_float4(v[0], v[1], v[2], v[3]);
+  f.b = make_float4(v[4], v[5], v[6], v[7]);
+  return f;
+}
+
+__device__ inline Frag<float> frag8(const float (&x)[16], int u) {
+  Frag<float> f;
+  f.a = make_float4(x[8 * u], x[8 * u + 1], x[8 * u + 2], x[8 * u + 3]);
+  f.b = make_float4(x[8 * u + 4], x[8 * u + 5], x[8 * u + 6], x[8 * u + 7]);
+  return f;
+}
+
+// dQ over CSR rows, 32-key steps: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T, dQ^T += K^T dS^T.
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void dq_f32_kernel(BwdArgs a) {
+  constexpr int kQk = D / 16, kOut = D / 32;
+  const int N = a.N, Nb = a.Nb, H = a.H;
+  const int total_rows = a.B * H * Nb;
+  const int pos = xcd_row(blockIdx.x, total_rows);
+  const int row = a.order ? __builtin_amdgcn_readfirstlane(a.order[pos]) : pos;
+  const int bh = row / Nb, r = row - bh * Nb, h = bh % H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int qn = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const int qi = r * BLK + w * 32 + qn;
+  const float* Q = static_cast<const float*>(a.q) + head;
+  const float* K = static_cast<const float*>(a.k) + head;
+  const float* V = static_cast<const float*>(a.v) + head;
+  const float* dO = static_cast<const float*>(a.dout) + head;
+
+  const int e0 = __builtin_amdgcn_readfirstlane(a.row_ptr[row]);
+  int e1 = __builtin_amdgcn_readfirstlane(a.row_ptr[row + 1]);
+  if ((a.skip_bits[h >> 5] >> (h & 31)) & 1u) e1 = e0;
+
+  f32x16_t acc[kOut];
+#pragma unroll
+  for (int io = 0; io < kOut; ++io) acc[io] = f32x16_t{};
+  if (e1 > e0) {
+    const int qr = min(qi, N - 1);
+    float lse2 = INFINITY, dd = 0.f;   // a query past N: +inf makes every weight 0
+    if (qi < N) {
+      const float2 p = *reinterpret_cast<const float2*>(a.ld + 2 * ((size_t)bh * N + qi));
+      lse2 = p.x;
+      dd = p.y;
+    }
+    Frag<float> qf[kQk];
+#pragma unroll
+    for (int t = 0; t < kQk; ++t) qf[t] = lds_frag(Q + (size_t)qr * D + 16 * t + 8 * hf);
+    for (int e = e0; e < e1; ++e) {
+      const int c = __builtin_amdgcn_readfirstlane(a.col_idx[e]);
+      const int nkv = min(BLK, N - c * BLK);
+      for (int k0 = 0; k0 < nkv; k0 += 32) {
+        const int nv = min(32, nkv - k0);
+        const float* kb = K + (size_t)(c * BLK + k0) * D;
+        const float* vb = V + (size_t)(c * BLK + k0) * D;
+        const int kr = min(qn, nv - 1);
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+        for (int t = 0; t < kQk; ++t) {
+          mma_k16(s, lds_frag(kb + (size_t)kr * D + 16 * t + 8 * hf), qf[t]);
+          mma_k16(dp, lds_frag(vb + (size_t)kr * D + 16 * t + 8 * hf),
+                  lds_frag(dO + (size_t)qr * D + 16 * t + 8 * hf));
+        }
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+          const float p = key < nv ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -lse2)) : 0.f;
+          ds[i] = p * (dp[i] - dd);
+        }
+#pragma unroll
+        for (int io = 0; io < kOut; ++io)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) mma_k16(acc[io], col_frag<D>(kb, 16 * u, hf, nv - 1, 32 * io + qn), frag8(ds, u));
+      }
+    }
+  }
+  if (qi < N) store_rows<kOut, D>(a.dq + head + (size_t)qi * D, acc, a.scale, hf);
+}
+
+// dK, dV over the transposed mask, 32-query steps: S = Q K^T, dP = dO V^T, P, dS,
+// dV^T += dO^T P, dK^T += Q^T dS (32 keys per wavefront, one key per lane column).
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void dkv_f32_kernel(BwdArgs a) {
+  constexpr int kQk = D / 16, kOut = D / 32;
+  const int N = a.N, Nb = a.Nb, H = a.H;
+  const int total = a.B * H * Nb;
+  const int col = __builtin_amdgcn_readfirstlane(a.col_order[xcd_row(blockIdx.x, total)]);
+  const int bh = col / Nb, c = col - bh * Nb, h = bh % H;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int qn = lane & 31, hf = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const int kk = c * BLK + w * 32 + qn;
+  const float* Q = static_cast<const float*>(a.q) + head;
+  const float* K = static_cast<const float*>(a.k) + head;
+  const float* V = static_cast<const float*>(a.v) + head;
+  const float* dO = static_cast<const float*>(a.dout) + head;
+  const float* ld = a.ld + 2 * (size_t)bh * N;
+
+  const int f0 = __builtin_amdgcn_readfirstlane(a.col_ptr[col]);
+  int f1 = __builtin_amdgcn_readfirstlane(a.col_ptr[col + 1]);
+  if ((a.skip_bits[h >> 5] >> (h & 31)) & 1u) f1 = f0;
+
+  f32x16_t dk[kOut], dv[kOut];
+#pragma unroll
+  for (int io = 0; io < kOut; ++io) {
+    dk[io] = f32x16_t{};
+    dv[io] = f32x16_t{};
+  }
+  if (f1 > f0) {
+    const int kr = min(kk, N - 1);   // keys past N: any finite row (their outputs are not stored)
+    Frag<float> kf[kQk];
+#pragma unroll
+    for (int t = 0; t < kQk; ++t) kf[t] = lds_frag(K + (size_t)kr * D + 16 * t + 8 * hf);
+    for (int f = f0; f < f1; ++f) {
+      const int r = __builtin_amdgcn_readfirstlane(a.row_idx[f]);
+      const int nqb = min(BLK, N - r * BLK);
+      for (int q0 = 0; q0 < nqb; q0 += 32) {
+        const int nq = min(32, nqb - q0);
+        const int qg = r * BLK + q0;
+        const float* qb = Q + (size_t)qg * D;
+        const float* gb = dO + (size_t)qg * D;
+        const int qr = min(qn, nq - 1);
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+        for (int t = 0; t < kQk; ++t) {
+          mma_k16(s, lds_frag(qb + (size_t)qr * D + 16 * t + 8 * hf), kf[t]);
+          mma_k16(dp, lds_frag(gb + (size_t)qr * D + 16 * t + 8 * hf),
+                  lds_frag(V + (size_t)kr * D + 16 * t + 8 * hf));
+        }
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = 8 * (i >> 2) + 4 * hf + (i & 3);
+          float p = 0.f, dsi = 0.f;
+          if (q < nq) {
+            const float2 l = *reinterpret_cast<const float2*>(ld + 2 * (size_t)(qg + q));
+            p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], a.scale_log2, -l.x));
+            dsi = p * (dp[i] - l.y);
+          }
+          pv[i] = p;
+          dsv[i] = dsi;
+        }
+#pragma unroll
+        for (int io = 0; io < kOut; ++io)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            mma_k16(dv[io], col_frag<D>(gb, 16 * u, hf, nq - 1, 32 * io + qn), frag8(pv, u));
+            mma_k16(dk[io], col_frag<D>(qb, 16 * u, hf, nq - 1, 32 * io + qn), frag8(dsv, u));
+          }
+      }
+    }
+  }
+  if (kk < N) {
+    store_rows<kOut, D>(a.dk + head + (size_t)kk * D, dk, a.scale, hf);
+    store_rows<kOut, D>(a.dv + head + (size_t)kk * D, dv, 1.f, hf);
+  }
+}
+
 template <int D, int BLK>
 hipError_t launch_grads(const BwdArgs& a, hipStream_t s) {
   const int rows = a.B * a.H * a.Nb;
-  hipLaunchKernelGGL((dq_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
+  if (a.in_f32)
+    hipLaunchKernelGGL((dq_f32_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
+  if (a.in_f32)
+    hipLaunchKernelGGL((dkv_f32_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL((dkv_kernel<D, BLK>), dim3((unsigned)rows), dim3(BLK * 2), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename TG, int D>
+void launch_prep(const BwdArgs& a, dim3 grid, size_t nq, hipStream_t s) {
+  if (a.o_bf16)
+    hipLaunchKernelGGL((bwd_prep_kernel<TG, uint16_t, D>), grid, dim3(256), 0, s,
+                       static_cast<const TG*>(a.dout), static_cast<const uint16_t*>(a.o), a.lse, a.ld, nq);
+  else
+    hipLaunchKernelGGL((bwd_prep_kernel<TG, float, D>), grid, dim3(256), 0, s,
+                       static_cast<const TG*>(a.dout), static_cast<const float*>(a.o), a.lse, a.ld, nq);
 }
 
 }  // namespace
@@ -654,21 +852,10 @@ hipError_t launch_attention_bwd(const BwdArgs& a, hipStream_t s) {
   const size_t nq = (size_t)a.B * a.H * a.N;
   const size_t threads = nq * (size_t)(a.d / 8);
   const dim3 pgrid((unsigned)((threads + 255) / 256));
-  if (a.d == 128) {
-    if (a.o_bf16)
-      hipLaunchKernelGGL((bwd_prep_kernel<uint16_t, 128>), pgrid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.o), a.lse, a.ld, nq);
-    else
-      hipLaunchKernelGGL((bwd_prep_kernel<float, 128>), pgrid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(a.dout), static_cast<const float*>(a.o), a.lse, a.ld, nq);
-  } else {
-    if (a.o_bf16)
-      hipLaunchKernelGGL((bwd_prep_kernel<uint16_t, 64>), pgrid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.o), a.lse, a.ld, nq);
-    else
-      hipLaunchKernelGGL((bwd_prep_kernel<float, 64>), pgrid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(a.dout), static_cast<const float*>(a.o), a.lse, a.ld, nq);
-  }
+  if (a.in_f32)
+    a.d == 128 ? launch_prep<float, 128>(a, pgrid, nq, s) : launch_prep<float, 64>(a, pgrid, nq, s);
+  else
+    a.d == 128 ? launch_prep<uint16_t, 128>(a, pgrid, nq, s) : launch_prep<uint16_t, 64>(a, pgrid, nq, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(csc_kernel, dim3((unsigned)(a.B * a.H)), dim3(kCscThreads), 0, s, a.row_ptr, a.col_idx,

@@ -132,7 +132,8 @@ typedef struct asa_csr {
  * 1.2.0 added asa_pattern_search; 1.3.0 added asa_attention_fwd_split; 1.4.0 added
  * ASA_PAT_FRAME_TILE; 1.5.0: asa_attention_bwd follows asa_csr.order, and asa_csr_capacity
  * returns -1 for every shape the mask builders reject; 1.6.0 added asa_build_mask_noalloc;
- * 1.7.0: the schedule gives every XCD an equal share of each row-length class. */
+ * 1.7.0: the schedule gives every XCD an equal share of each row-length class; 1.8.0:
+ * asa_attention_bwd takes fp32 inputs. */
 int32_t asa_version(void);
 
 /* Human-readable name of a status code (static storage). */
@@ -310,11 +311,11 @@ size_t asa_attention_bwd_workspace_size(const asa_shape* shape);
  *   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . V_j,   D_i = dO_i . O_i,
  *   dS_ij = P_ij (dP_ij - D_i),   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i.
  * dQ sums over each row's kept key blocks; dK and dV over the query blocks that keep each
- * key block (the transposed mask, built in the workspace).  P and dS are rounded to bf16
- * for the matrix products; all accumulation is fp32.  Deterministic (no atomics).
+ * key block (the transposed mask, built in the workspace).  With bf16 inputs P and dS are
+ * rounded to bf16 for the matrix products; with fp32 inputs they stay fp32 (fp32 matrix
+ * products).  All accumulation is fp32.  Deterministic (no atomics).
  *
- * Q, K, V, dO  device [B,H,N,d] bf16 (shape->in_dtype must be ASA_BF16; ASA_F32 inputs
- *              return ASA_ERR_UNSUPPORTED).
+ * Q, K, V, dO  device [B,H,N,d] of shape->in_dtype (ASA_BF16 or ASA_F32).
  * O            device [B,H,N,d] of o_dtype: the forward's output for the same inputs.
  * lse          device float32 [B,H,N] from asa_attention_fwd_lse for the same inputs.
  * dQ, dK, dV   device float32 [B,H,N,d], fully written (zero where no kept tile

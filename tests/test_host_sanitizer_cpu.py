@@ -124,8 +124,8 @@ int main(void) {
 
   /* asa_attention_bwd */
   size_t bneed = asa_attention_bwd_workspace_size(&s);
-  EXPECT(asa_attention_bwd(F, F, F, F, ASA_F32, F, (float*)F, (float*)F, (float*)F, (float*)F, &f32, &csr, NULL,
-                           0.f, W, bneed, NULL), ASA_ERR_UNSUPPORTED);
+  EXPECT(asa_attention_bwd(F, F, F, F, ASA_F32, F, NULL, (float*)F, (float*)F, (float*)F, &f32, &csr, NULL,
+                           0.f, W, bneed, NULL), ASA_ERR_NULL_ARG);
   EXPECT(asa_attention_bwd(F, F, F, F, ASA_F32, F, NULL, (float*)F, (float*)F, (float*)F, &s, &csr, NULL, 0.f, W,
                            bneed, NULL), ASA_ERR_NULL_ARG);
   EXPECT(asa_attention_bwd(F, F, F, F, 3, F, (float*)F, (float*)F, (float*)F, (float*)F, &s, &csr, NULL, 0.f, W,
