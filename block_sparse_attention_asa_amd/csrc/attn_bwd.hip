@@ -220,7 +220,7 @@ __device__ inline void store_rows(float* row, const f32x16_t (&acc)[kOut], float
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) void dq_kernel(BwdArgs a) {
   using T = uint16_t;
-  constexpr int KT = 64;
+  constexpr int KT = (D == 128 && BLK == 64) ? 32 : 64;
   constexpr int kSteps = BLK / KT;
   constexpr int kWaves = BLK / 32;
   constexpr int NT = 64 * kWaves;
