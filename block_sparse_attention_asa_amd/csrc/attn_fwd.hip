@@ -38,10 +38,11 @@ namespace {
 // instantiation keeps the registers of the plain kernel untouched.
 // KT: keys per step.  32-key steps keep a d = 128 kernel under 168 registers and 32 KB of
 // LDS, so three wavefronts share a SIMD; launches with enough rows to fill those slots use
-// them.  64-key steps do more work per barrier, which wins when a compute unit holds fewer
-// workgroups (small launches, d = 64).
+// them (128-query blocks), as do all d = 128 launches with 64-query blocks (two wavefronts
+// per SIMD there).  64-key steps do more work per barrier, which wins when a compute unit
+// holds fewer workgroups (small launches, d = 64).
 template <typename T, typename TO, int D, int BLK, int KT, bool kSplit>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 32 ? 3 : 2))) void attn_fwd_kernel(
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(KT == 32 && BLK == 128 ? 3 : 2))) void attn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, TO* __restrict__ O,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx, int H, int N, int Nb,
     int total_rows, float scale_log2, AttnArgs meta) {
@@ -520,6 +521,12 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t s) {
   if constexpr (D == 128 && BLK == 128) {
     if ((long long)a.B * a.H * a.Nb >= kShortStepRows) return launch_kt<T, TO, D, BLK, 32>(a, s);
   }
+  // d = 128 with 64-query blocks: two wavefronts per workgroup, so a 64-key step costs each
+  // thread twice the transfers of a 128-block launch, and the kernel ran at one wavefront per
+  // SIMD.  32-key steps fit two wavefronts without spills; LDS (32 KB per two-wavefront
+  // workgroup) holds five workgroups per compute unit, so a three-wavefront register target
+  // would only add spills.
+  if constexpr (D == 128 && BLK == 64) return launch_kt<T, TO, D, BLK, 32>(a, s);
   return launch_kt<T, TO, D, BLK, 64>(a, s);
 }
 
