@@ -1,13 +1,15 @@
 """GPU parity on seeded random configurations: the mask builders (adaptive and static-only),
-the forward (with lse), the split-row forward, the pattern search and, for bf16 inputs, the
-backward, against the float64 oracle.
+the forward (with lse), the split-row forward, the pattern search and the backward, against
+the float64 oracle.
 
 Each case draws B, H, N (ragged tails and single-block sequences included), d, blk, input
 dtype and structure, top-k or tau (with and without a cap), text tokens, the diagonal, and
 per-head static patterns (full, skip, diagonal, multi-diagonal, vertical stripe, frame
 tiles, adaptive).  The bounds are the suite's own: CSR bit-exact outside ambiguous rows;
 forward 2e-2 max / 2e-3 mean absolute (bf16 inputs), 1e-4 (fp32 inputs); lse within
-2^-8 + 1e-4; gradients within 2e-2 of the largest and 5e-3 of the mean reference entry.
+2^-8 + 1e-4; gradients within 2e-2 of the largest and 5e-3 of the mean reference entry (bf16
+inputs), and within 2^-12 of each element's product sums plus 2^-14 of the largest entry
+(fp32 inputs).
 The GPU attends the oracle's own mask, so no oracle input comes from the HIP path.
 """
 import numpy as np
@@ -59,6 +61,19 @@ def _grad_close(got, want, label):
     say(f"  [{label}] max abs err {err.max():.3e} (ref max {smax:.3e})  mean {err.mean():.3e} (ref mean {smean:.3e})")
     assert err.max() <= GRAD_MAX_REL * smax + 1e-6, label
     assert err.mean() <= GRAD_MEAN_REL * smean + 1e-7, label
+
+
+def _grad_close_f32(got, ref, terms, label):
+    """fp32 inputs: 2^-12 of each element's product sums plus 2^-14 of the gradient's scale
+    (the bound of test_gpu_backward_f32, derived there); exact zeros where nothing adds."""
+    from test_gpu_backward_f32 import SCALE_REL, TERMS_REL
+    a = got.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(a)), f"{label}: non-finite gradient"
+    err = np.abs(a - ref)
+    bound = TERMS_REL * terms + SCALE_REL * float(np.abs(ref).max())
+    assert np.all(err <= bound), f"{label} (fp32): {int((err > bound).sum())} elements over the rounding bound"
+    zero = ref == 0.0
+    assert np.all(a[zero] == 0.0), f"{label} (fp32): nonzero gradient where no tile contributes"
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
@@ -146,6 +161,16 @@ def test_random_config(asa_lib, seed):
         _grad_close(dq, rdq, "dQ")
         _grad_close(dk, rdk, "dK")
         _grad_close(dv, rdv, "dV")
+    if cfg.dtype == "f32" and Meff.any():
+        g = np.random.default_rng(seed).standard_normal(tuple(x["q"].shape)).astype(np.float32)
+        grads = asa.asa_attention_bwd(xd["q"], xd["k"], xd["v"], out, torch.from_numpy(g).to("cuda:0"), lse, rp_o,
+                                      ci_o, cfg.blk, patterns=cfg.patterns)
+        torch.cuda.synchronize()
+        g64 = g.astype(np.float64)
+        refs = O.attention_bwd(q64, k64, v64, g64, Meff, cfg.blk)
+        terms = O.attention_bwd_terms(q64, k64, v64, g64, Meff, cfg.blk)
+        for got, ref, t, label in zip(grads, refs, terms, ("dQ", "dK", "dV")):
+            _grad_close_f32(got, ref, t, label)
 
 
 # Launches of at least 768 query-block rows at d = 128, blk = 128 take the 32-key-step
