@@ -618,8 +618,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2))) vo
 // ------------------------------------------------------------------ fp32 inputs
 // fp32 Q, K, V and dO: the same products on the fp32 matrix cores (eight
 // v_mfma_f32_32x32x2f32 per 16-wide k-step, through mma_k16) with P and dS kept in fp32.
-// One such product does 4096 flops for 512 bytes of operands at an eighth of the bf16
-// product's rate, so operand traffic is no constraint here: every wavefront reads its
+// One such product does 4096 flops for 512 bytes of operands in 64 cycles, a sixteenth of
+// the bf16 flop rate, so operand traffic is no constraint here: every wavefront reads its
 // fragments straight from global memory (the wavefronts of a workgroup share them through
 // the caches), with no LDS staging and no barriers.  Reads of keys or queries past N are
 // clamped to the last valid row of the block, and those elements get weight 0.

@@ -522,10 +522,10 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t s) {
     if ((long long)a.B * a.H * a.Nb >= kShortStepRows) return launch_kt<T, TO, D, BLK, 32>(a, s);
   }
   // d = 128 with 64-query blocks: two wavefronts per workgroup, so a 64-key step costs each
-  // thread twice the transfers of a 128-block launch, and the kernel ran at one wavefront per
-  // SIMD.  32-key steps fit two wavefronts without spills; LDS (32 KB per two-wavefront
-  // workgroup) holds five workgroups per compute unit, so a three-wavefront register target
-  // would only add spills.
+  // thread twice the transfers of a 128-block launch and more registers than two wavefronts
+  // per SIMD leave.  32-key steps fit two wavefronts without spills; LDS (32 KB per
+  // two-wavefront workgroup) holds five workgroups per compute unit, so a three-wavefront
+  // register target would only add spills.
   if constexpr (D == 128 && BLK == 64) return launch_kt<T, TO, D, BLK, 32>(a, s);
   return launch_kt<T, TO, D, BLK, 64>(a, s);
 }
