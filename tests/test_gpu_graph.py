@@ -14,21 +14,25 @@ from gpu_helpers import say, to_device
 pytestmark = pytest.mark.gpu
 
 
-def test_captured_step_replays_match_eager(asa_lib):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_captured_step_replays_match_eager(asa_lib, dtype):
+    """bf16 inputs take the LDS-ring kernels of both passes; fp32 inputs take the fp32
+    matrix-core backward, which reads its operands straight from global memory."""
     asa = asa_lib
     cfg = gen.scaled(gen.WAN, H=2, frames=2)
     cfg.k = 4
     B, H, N, d, blk = cfg.B, cfg.H, cfg.N, cfg.d, cfg.blk
-    say(f"case {cfg.name}: graph capture of mask build + forward + backward")
+    say(f"case {cfg.name} ({dtype}): graph capture of mask build + forward + backward")
     dev = torch.device("cuda:0")
-    x = to_device(gen.make_inputs(cfg))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = {k: v.to(tdt) for k, v in to_device(gen.make_inputs(cfg)).items()}
     g = torch.Generator().manual_seed(11)
-    dout = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16).to(dev)
+    dout = torch.randn((B, H, N, d), generator=g).to(tdt).to(dev)
     rows = B * H * cfg.Nb
     rp = torch.empty(rows + 1, dtype=torch.int32, device=dev)
     ci = torch.empty(asa.asa_csr_capacity(B, H, N, blk), dtype=torch.int32, device=dev)
     order = torch.empty(rows, dtype=torch.int32, device=dev)
-    shp = asa.asa_shape(B, H, N, d, blk, asa.ASA_BF16)
+    shp = asa.asa_shape(B, H, N, d, blk, asa.ASA_BF16 if dtype == "bf16" else asa.ASA_F32)
     import ctypes
     mws = torch.empty(int(asa.lib.asa_build_mask_workspace_size(ctypes.byref(shp))), dtype=torch.uint8, device=dev)
     bws = torch.empty(int(asa.lib.asa_attention_bwd_workspace_size(ctypes.byref(shp))), dtype=torch.uint8, device=dev)
